@@ -1,0 +1,123 @@
+/*
+ * nvfp4_gg.h -- C ABI of the MI355X (gfx950) NVFP4 grouped GEMM.
+ *
+ * Operation (per group i = 0..g-1):
+ *
+ *   C_i[m_i x n] (fp16) = dequant(A_i[m_i x k]) * dequant(B_i[n x k])^T,  fp32 accumulation,
+ *
+ * where dequant(X)[r][kk] = e2m1(X[r][kk]) * e4m3fn(SFX[r][kk / 16]).  This is the
+ * operation of the leaderboard task nvfp4_group_gemm: the custom_kernel docstring of the
+ * page "kernelindex submission 503584" gives the operands (a[m, k/2] and b[n, k/2] of
+ * packed FP4 E2M1 codes, sfa[m, k/16] and sfb[n, k/16] of FP8 E4M3 scales, c[m, n] fp16,
+ * one (m, n, k) problem per group), its kernel configuration block the data types
+ * (Float4E2M1FN, Float8E4M3FN, 16 elements per scale, Float16 output, Float32
+ * accumulator) and the comment before its launch the product "C = A * SFA * B * SFB".
+ * Output rounding is round-to-nearest-even, as in the epilogue_store function of the page
+ * "kernelindex submission 498317".
+ *
+ * Data layout (all row-major, no batch dimension):
+ *   A_i   [m_i][k/2] bytes: two E2M1 codes per byte along K, low nibble = even K index.
+ *   B_i   [n  ][k/2] bytes: same packing.
+ *   SFA_i [m_i][k/16] bytes: E4M3FN codes (finite; 0x7F/0xFF are NaN and not supported).
+ *   SFB_i [n  ][k/16] bytes: E4M3FN codes.
+ *   C_i   [m_i][n] fp16 (IEEE binary16).
+ * n and k are the same for every group; m_i varies (m_i = 0 is allowed and writes nothing).
+ *
+ * Ownership: the caller owns every device buffer.  A plan owns host memory only.
+ * Asynchrony: nvfp4_gg_run only enqueues work on the given stream; it never synchronises,
+ * allocates device memory, prints or throws.
+ * Threading: a plan is immutable after nvfp4_gg_plan returns; several threads may call
+ * nvfp4_gg_run on one plan concurrently.  Distinct plans are independent.
+ * Errors: every entry point returns a status code; nothing is thrown across this ABI.
+ */
+#ifndef NVFP4_GG_H
+#define NVFP4_GG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest number of groups one plan accepts: the whole per-group table travels in the
+ * kernel arguments (no device allocation, no host-to-device copy per call). */
+#define NVFP4_GG_MAX_GROUPS 64
+
+/* Pass as `device` to nvfp4_gg_plan to build a plan for a nominal MI355X (256 compute
+ * units) without touching the HIP runtime.  Such a plan can be inspected with
+ * nvfp4_gg_plan_info but nvfp4_gg_run rejects it with NVFP4_GG_EUNSUPPORTED. */
+#define NVFP4_GG_DEVICE_NONE (-2)
+
+typedef enum {
+    NVFP4_GG_OK = 0,
+    NVFP4_GG_EINVAL = 1,       /* bad argument: null pointer, bad size, unknown plan */
+    NVFP4_GG_EALIGN = 2,       /* a device pointer is not 16-byte aligned */
+    NVFP4_GG_ENOMEM = 3,       /* host allocation failed */
+    NVFP4_GG_EHIP = 4,         /* a HIP runtime call failed (device query or launch) */
+    NVFP4_GG_EUNSUPPORTED = 5  /* device is not gfx950, g too large, or a host-only plan */
+} nvfp4_gg_status_t;
+
+typedef struct nvfp4_gg_plan_s* nvfp4_gg_plan_t;
+
+/* What a plan decided; filled by nvfp4_gg_plan_info. */
+typedef struct {
+    int g, n, k;
+    int device;            /* HIP device ordinal, or NVFP4_GG_DEVICE_NONE */
+    int num_cus;           /* compute units the schedule was sized for */
+    int tile_m, tile_n;    /* output tile of one workgroup */
+    int total_tiles;       /* tiles over all groups */
+    int grid;              /* workgroups launched per call */
+    int block;             /* threads per workgroup */
+    int lds_bytes;         /* LDS per workgroup */
+    int variant;           /* kernel variant id (see the design notes) */
+    int order[NVFP4_GG_MAX_GROUPS];       /* group processed at schedule position p */
+    int tile_begin[NVFP4_GG_MAX_GROUPS + 1]; /* exclusive tile prefix in schedule order */
+} nvfp4_gg_plan_info_t;
+
+/*
+ * Build a plan for g groups with row counts m[0..g-1] (host array, copied), and shared
+ * n and k.  Host-only work: validation, per-group tile counts, the largest-work-first
+ * group order and its tile prefix sum (the host planning of custom_kernel on the page
+ * "kernelindex submission 503584": groups sorted by tile work, prefix of per-group tile
+ * counts), and the launch shape.
+ *   device: HIP device ordinal, -1 for the current device, or NVFP4_GG_DEVICE_NONE.
+ * Requirements: 1 <= g <= NVFP4_GG_MAX_GROUPS, n >= 1, k >= 256 and k % 256 == 0 (the
+ * K granularity the group_gemm host function of "kernelindex submission 498317"
+ * requires), 0 <= m_i <= 2^20; else NVFP4_GG_EINVAL (g above the maximum:
+ * NVFP4_GG_EUNSUPPORTED).  A device that is not gfx950: NVFP4_GG_EUNSUPPORTED.
+ * On success *out holds a new plan, released with nvfp4_gg_destroy; on failure *out = NULL.
+ */
+nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
+                                int device);
+
+/*
+ * Enqueue one grouped GEMM on `stream` (0 = the null stream of the plan's device).
+ * A, B, SFA, SFB, C: host arrays of g device pointers (read before returning; the caller
+ * may reuse the arrays at once), in the caller's group order.  Every pointer of a group
+ * with m_i > 0 must be non-null (else NVFP4_GG_EINVAL) and 16-byte aligned (else
+ * NVFP4_GG_EALIGN); pointers of groups with m_i = 0 are ignored.  C must not overlap any
+ * input.  Each element of every C_i[m_i x n] is written exactly once; nothing else is
+ * written and C is never read.  The current HIP device must be the plan's device
+ * (else NVFP4_GG_EINVAL).  A failed launch returns NVFP4_GG_EHIP.
+ */
+nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan,
+                               const void* const* A, const void* const* B,
+                               const void* const* SFA, const void* const* SFB,
+                               void* const* C, hipStream_t stream);
+
+/* Copy the plan's decisions into *info.  NVFP4_GG_EINVAL on a null argument. */
+nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_plan_info_t* info);
+
+/* Release a plan (NULL is ignored).  Work already enqueued by nvfp4_gg_run is unaffected. */
+void nvfp4_gg_destroy(nvfp4_gg_plan_t plan);
+
+/* Static English text for a status code; never NULL. */
+const char* nvfp4_gg_status_string(nvfp4_gg_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_GG_H */

@@ -124,6 +124,7 @@ def ulp16(ref_bits: np.ndarray) -> np.ndarray:
     """Spacing of fp16 at the oracle's fp16 value: 2^(max(floor(log2|x|), -14) - 10);
     the spacing at 0 and in the subnormal range is 2^-24."""
     x = np.abs(ref_bits.view(np.float16).astype(np.float64))
+    x = np.where(np.isfinite(x), x, 65504.0)   # Inf/NaN: spacing of the top binade
     with np.errstate(divide="ignore"):
         e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
     e = np.where(x > 0, np.maximum(e, -14.0), -14.0)

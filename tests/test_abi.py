@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and
+its host-side validation and planning behave as include/nvfp4_gg.h documents."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import precision_moe_nvfp4_amd as gg
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "nvfp4_gg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:nvfp4_gg_status_t|void|const char\s*\*)\s*(nvfp4_gg_\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) == {
+        "nvfp4_gg_plan", "nvfp4_gg_run", "nvfp4_gg_plan_info", "nvfp4_gg_destroy", "nvfp4_gg_status_string"}
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", gg.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(gg.library(), name) is not None
+
+
+def test_status_strings():
+    for st in range(6):
+        s = gg.nvfp4_gg_status_string(st)
+        assert s and s != "unknown status"
+    assert gg.nvfp4_gg_status_string(99) == "unknown status"
+
+
+def raw_plan(g, m, n, k, device=gg.DEVICE_NONE):
+    out = ctypes.c_void_p(1234)
+    marr = (ctypes.c_int * max(len(m), 1))(*m) if m is not None else None
+    st = gg.library().nvfp4_gg_plan(ctypes.byref(out), g, marr, n, k, device)
+    return st, out.value
+
+
+@pytest.mark.parametrize("g,m,n,k", [
+    (0, [], 64, 256), (1, [4], 0, 256), (1, [4], 64, 128), (1, [4], 64, 300), (1, [4], 64, 0),
+    (1, [-1], 64, 256), (1, None, 64, 256), (2, [1, (1 << 20) + 1], 64, 256),
+])
+def test_plan_rejects_bad_arguments(g, m, n, k):
+    st, handle = raw_plan(g, m, n, k)
+    assert st == gg.EINVAL and handle is None
+
+
+def test_plan_limits():
+    st, handle = raw_plan(65, [1] * 65, 64, 256)
+    assert st == gg.EUNSUPPORTED and handle is None
+    st, handle = raw_plan(1, [1], 64, 256, device=-3)
+    assert st == gg.EINVAL
+    st = gg.library().nvfp4_gg_plan(None, 1, (ctypes.c_int * 1)(1), 64, 256, gg.DEVICE_NONE)
+    assert st == gg.EINVAL
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    ([80, 176, 128, 72, 64, 248, 96, 160], 4096, 7168),
+    ([40, 76, 168, 72, 164, 148, 196, 160], 7168, 2048),
+    ([128, 384], 4096, 1536), ([0, 5, 0, 300], 200, 256), ([64] * 64, 256, 512)])
+def test_host_plan_order_and_tile_prefix(m, n, k):
+    plan = gg.nvfp4_gg_plan(m, n, k, device=gg.DEVICE_NONE)
+    info = gg.nvfp4_gg_plan_info(plan)
+    g = len(m)
+    assert (info.g, info.n, info.k, info.device, info.num_cus) == (g, n, k, gg.DEVICE_NONE, 256)
+    order = list(info.order)[:g]
+    assert sorted(order) == list(range(g))
+    # largest group first, ties keep the caller order
+    assert order == sorted(range(g), key=lambda i: (-m[i], i))
+    tiles = [ceil_div(m[i], info.tile_m) * ceil_div(n, info.tile_n) for i in order]
+    prefix = [0]
+    for t in tiles:
+        prefix.append(prefix[-1] + t)
+    assert list(info.tile_begin)[:g + 1] == prefix
+    assert info.total_tiles == prefix[-1]
+    assert info.grid >= 1 if prefix[-1] else info.grid == 0
+    assert info.block % 64 == 0 and 0 < info.lds_bytes <= 160 * 1024
+
+
+def test_run_validates_pointers_before_touching_the_device():
+    m, n, k = [4, 0], 64, 256
+    plan = gg.nvfp4_gg_plan(m, n, k, device=gg.DEVICE_NONE)
+    ok = [0x10000, 0]            # group 1 has m = 0: its pointers are ignored
+    # every pointer valid -> validation passes, then the host-only plan is refused
+    with pytest.raises(gg.Nvfp4GGError) as e:
+        gg.nvfp4_gg_run(plan, ok, ok, ok, ok, ok, stream=0)
+    assert e.value.status == gg.EUNSUPPORTED
+    with pytest.raises(gg.Nvfp4GGError) as e:
+        gg.nvfp4_gg_run(plan, [0, 0], ok, ok, ok, ok, stream=0)
+    assert e.value.status == gg.EINVAL
+    with pytest.raises(gg.Nvfp4GGError) as e:
+        gg.nvfp4_gg_run(plan, ok, [0x10008, 0], ok, ok, ok, stream=0)
+    assert e.value.status == gg.EALIGN
+    with pytest.raises(gg.Nvfp4GGError) as e:
+        gg.nvfp4_gg_run(plan, ok, ok, ok, ok, [0x10002, 0], stream=0)
+    assert e.value.status == gg.EALIGN
+    L = gg.library()
+    assert L.nvfp4_gg_run(ctypes.c_void_p(plan.handle), None, None, None, None, None, None) == gg.EINVAL
+    assert L.nvfp4_gg_run(None, None, None, None, None, None, None) == gg.EINVAL
+    gg.nvfp4_gg_destroy(plan)
+    gg.nvfp4_gg_destroy(plan)    # second destroy is a no-op on the Python side
+    L.nvfp4_gg_destroy(None)
+
+
+def test_plan_info_rejects_null():
+    L = gg.library()
+    assert L.nvfp4_gg_plan_info(None, None) == gg.EINVAL

@@ -1,0 +1,130 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Bar (per element): |gpu - ref| <= 2 ulp16(ref) + 1e-5 * sum_k |a*sa*b*sb|, with ref the
+oracle's fp16 value; infinities must match exactly.  Every C_i is surrounded by canary
+halves (a NaN pattern) to prove that each element is written exactly inside its bounds.
+The fp16 bit-mismatch count (expected 0: the fp32 sums of these inputs are exact) is
+printed as a diagnostic.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_moe_nvfp4_amd as gg
+from synthetic import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 0x7FFF      # an fp16 NaN pattern the kernel never produces
+PAD = 64             # canary halves before and after each C_i
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_gpu(inp, stream=None, plan=None):
+    dev = torch.device("cuda", 0)
+    A, B, SFA, SFB = gg.device_operands(inp.A, inp.B, inp.SFA, inp.SFB, dev)
+    bufs, views = [], []
+    for mi in inp.m:
+        buf = torch.full((PAD + mi * inp.n + PAD,), CANARY, dtype=torch.int16, device=dev)
+        bufs.append(buf)
+        views.append(buf[PAD:PAD + mi * inp.n])
+    if plan is None:
+        plan = gg.nvfp4_gg_plan(inp.m, inp.n, inp.k)
+    gg.nvfp4_gg_run(plan, A, B, SFA, SFB, views, stream=stream)
+    torch.cuda.synchronize()
+    out = []
+    for mi, buf in zip(inp.m, bufs):
+        h = buf.cpu().numpy().view(np.uint16)
+        assert np.all(h[:PAD] == CANARY) and np.all(h[PAD + mi * inp.n:] == CANARY), "write outside C_i"
+        out.append(h[PAD:PAD + mi * inp.n].reshape(mi, inp.n))
+    return out
+
+
+def check(inp, got, label):
+    ref = oracle.grouped_inputs(inp, want_abs=True)
+    total_bad = total_mis = total = 0
+    for i in range(inp.g):
+        g16, r16 = got[i], ref.C[i]
+        assert not np.any(g16 == CANARY), f"{label}: group {i} has unwritten elements"
+        gv = g16.view(np.float16).astype(np.float64)
+        rv = r16.view(np.float16).astype(np.float64)
+        inf = np.isinf(rv)
+        assert np.array_equal(np.isinf(gv), inf) and np.array_equal(gv[inf], rv[inf]), f"{label}: inf mismatch"
+        tol = oracle.tolerance(r16, ref.abssum[i])
+        err = np.abs(np.where(inf, 0.0, gv - np.where(inf, 0.0, rv)))
+        bad = err > tol
+        total_bad += int(bad.sum())
+        total_mis += int(np.sum((g16 != r16) & ((g16 | r16) & 0x7FFF != 0)))
+        total += g16.size
+        if bad.any():
+            r, c = np.argwhere(bad)[0]
+            say(f"{label}: group {i} first bad ({r},{c}) gpu={gv[r, c]} ref={rv[r, c]} tol={tol[r, c]}")
+    say(f"{label}: {total} elements, {total_bad} beyond tolerance, {total_mis} fp16 bit mismatches")
+    assert total_bad == 0
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
+def test_configs_full_size(name):
+    say(f"parity {name}: {CONFIGS[name]}")
+    inp = make_inputs(CONFIGS[name].m, CONFIGS[name].n, CONFIGS[name].k, CONFIGS[name].seed)
+    check(inp, run_gpu(inp), name)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    ([1], 16, 256), ([17, 1, 129], 200, 256), ([255, 0, 3], 130, 512), ([0, 0, 7], 64, 256),
+    ([300], 1, 768), ([33, 65, 97, 129, 161], 384, 1024), ([2] * 64, 48, 256), ([384, 500], 136, 256),
+])
+def test_ragged_and_edge_shapes(m, n, k):
+    say(f"parity ragged m={m} n={n} k={k}")
+    inp = make_inputs(m, n, k, seed=len(m) * 1000 + n + k)
+    check(inp, run_gpu(inp), f"ragged m={m} n={n} k={k}")
+
+
+def test_every_e4m3fn_code_and_negative_scales():
+    # scale codes over every finite E4M3FN code, including negative and subnormal ones
+    say("parity all scale codes")
+    m, n, k = [96, 40], 256, 512
+    inp = make_inputs(m, n, k, seed=77)
+    rng = np.random.default_rng(78)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    inp.SFA = [finite[rng.integers(0, len(finite), a.shape)] for a in inp.SFA]
+    inp.SFB = [finite[rng.integers(0, len(finite), b.shape)] for b in inp.SFB]
+    check(inp, run_gpu(inp), "all scale codes")
+
+
+def test_large_values_round_to_inf_like_the_oracle():
+    # scales near 448 push sums beyond fp16's range: both sides must give the same infinities
+    say("parity overflow")
+    m, n, k = [32], 64, 256
+    inp = make_inputs(m, n, k, seed=79, scale_lo=0x70, scale_hi=0x7E)
+    check(inp, run_gpu(inp), "overflow")
+
+
+def test_repeatable_and_stream_aware():
+    say("repeatability + side stream")
+    inp = make_inputs([100, 28], 512, 1024, seed=80)
+    plan = gg.nvfp4_gg_plan(inp.m, inp.n, inp.k)
+    first = run_gpu(inp, plan=plan)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        second = run_gpu(inp, stream=s, plan=plan)
+    for a, b in zip(first, second):
+        assert np.array_equal(a, b)
+    check(inp, first, "repeatable")
+
+
+def test_misaligned_pointer_is_rejected_on_device():
+    say("misaligned pointer")
+    inp = make_inputs([16], 64, 256, seed=81)
+    A, B, SFA, SFB = gg.device_operands(inp.A, inp.B, inp.SFA, inp.SFB, "cuda")
+    C = torch.empty(16 * 64 + 8, dtype=torch.float16, device="cuda")
+    plan = gg.nvfp4_gg_plan(inp.m, inp.n, inp.k)
+    with pytest.raises(gg.Nvfp4GGError) as e:
+        gg.nvfp4_gg_run(plan, A, B, SFA, SFB, [C.data_ptr() + 2])
+    assert e.value.status == gg.EALIGN
+    info = gg.nvfp4_gg_plan_info(plan)
+    assert info.device == torch.cuda.current_device() and info.num_cus > 0
