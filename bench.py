@@ -12,10 +12,10 @@ Timing protocol (per shape):
   * a second figure re-runs the same K calls as plain launches (host launch overhead
     included), and a third uses one input set only ("warm").
 The roofline object prices the kernel against the fp16 MFMA dense peak (the path's
-contraction runs on v_mfma_f32_16x16x32_f16) with the algorithmic flops per launch.
+contraction runs on v_mfma_f32_32x32x16_f16) with the algorithmic flops per launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes c1,c2,c3,c4]
-                       [--no-cpu-baseline] [--calibrate-copy]
+                       [--no-cpu-baseline] [--cold-only] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -69,11 +69,20 @@ def recorded_traffic():
     return float(t.group(1))
 
 
+def shape_of(name):
+    """A page workload by name, or a custom shape "m0/m1/...:n:k" (diagnostics only)."""
+    from synthetic import CONFIGS, GroupedShape
+    if name in CONFIGS:
+        return CONFIGS[name]
+    ms, n, k = name.split(":")
+    return GroupedShape(name, tuple(int(x) for x in ms.split("/")), int(n), int(k))
+
+
 def make_sets(torch, gg, name, R, dev):
     """Set 0 is the seeded numpy workload (identical to the parity tests); sets 1..R-1 are
     drawn on the device with the same distribution (uniform bytes, scale codes 0x08..0x20)."""
-    from synthetic import CONFIGS, SCALE_CODE_HI, SCALE_CODE_LO, make_inputs
-    cfg = CONFIGS[name]
+    from synthetic import SCALE_CODE_HI, SCALE_CODE_LO, make_inputs
+    cfg = shape_of(name)
     inp = make_inputs(cfg.m, cfg.n, cfg.k, cfg.seed)
     sets = []
     A, B, SFA, SFB = gg.device_operands(inp.A, inp.B, inp.SFA, inp.SFB, dev)
@@ -90,9 +99,8 @@ def make_sets(torch, gg, name, R, dev):
     return cfg, sets, Cs
 
 
-def time_shape(torch, gg, name, steps, warmup, dev):
-    from synthetic import CONFIGS
-    cfg = CONFIGS[name]
+def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False):
+    cfg = shape_of(name)
     nbytes = algorithmic_bytes(cfg.m, cfg.n, cfg.k)
     flops = algorithmic_flops(cfg.m, cfg.n, cfg.k)
     R = max(1, math.ceil(COLD_BYTES / nbytes))
@@ -140,13 +148,13 @@ def time_shape(torch, gg, name, steps, warmup, dev):
         return e0.elapsed_time(e1) * 1000.0 / len(seq)
 
     us_cold = graph_time(cold_seq)
-    us_direct = direct_time(cold_seq)
-    us_warm = graph_time(warm_seq)
+    us_direct = None if cold_only else direct_time(cold_seq)
+    us_warm = None if cold_only else graph_time(warm_seq)
     t_roof_us = max(nbytes / (PEAK_HBM_GBS * 1e3), flops / (PEAK_F16_TFLOPS * 1e6))
     res = {
         "us_per_call": round(us_cold, 3),
-        "us_per_call_direct_launch": round(us_direct, 3),
-        "us_per_call_warm": round(us_warm, 3),
+        "us_per_call_direct_launch": None if us_direct is None else round(us_direct, 3),
+        "us_per_call_warm": None if us_warm is None else round(us_warm, 3),
         "eff_tflops": round(flops / us_cold / 1e6, 1),
         "eff_hbm_tbs": round(nbytes / us_cold / 1e6, 3),
         "algorithmic_bytes": nbytes,
@@ -203,6 +211,9 @@ def main():
     ap.add_argument("--shapes", default="c1,c2,c3,c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="time only the cold graph replays (for profiler runs whose kernel "
+                         "average should match the reported value)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: --gpus {a.gpus} is not supported: this NVFP4 grouped GEMM runs on one GPU "
@@ -225,8 +236,8 @@ def main():
         names.insert(0, HEADLINE)
     shapes = {}
     for nm in names:
-        print(f"bench: timing {nm} {CONFIGS[nm]}", file=sys.stderr, flush=True)
-        shapes[nm] = time_shape(torch, gg, nm, a.steps, a.warmup, dev)
+        print(f"bench: timing {nm} {shape_of(nm)}", file=sys.stderr, flush=True)
+        shapes[nm] = time_shape(torch, gg, nm, a.steps, a.warmup, dev, cold_only=a.cold_only)
         print(f"bench: {nm} -> {shapes[nm]}", file=sys.stderr, flush=True)
     head = shapes[HEADLINE]
     cfg = CONFIGS[HEADLINE]

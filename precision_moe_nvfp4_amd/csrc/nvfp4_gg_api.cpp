@@ -30,6 +30,8 @@ struct nvfp4_gg_plan_s {
     int total_tiles;
     int grid;
     std::vector<int> m;          // caller order
+    std::vector<int> tiles_m;    // m chunks per group, caller order
+    std::vector<int> rows_per;   // rows per m chunk, caller order
     std::vector<int> order;      // order[p] = caller group at schedule position p
     std::vector<int> tile_begin; // size g + 1, schedule order
 };
@@ -89,15 +91,22 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const in
         p->k = k;
         p->device = device;
         p->num_cus = num_cus;
-        p->variant = kVariantTiled128;
+        p->variant = kVariantRing;
         p->shape = variant_shape(p->variant);
         p->m.assign(m, m + g);
+        p->tiles_m.assign(g, 0);
+        p->rows_per.assign(g, 0);
 
-        // tile counts per group and the largest-work-first order (stable for ties)
+        // m chunks: as few as the tile height allows, equal sizes rounded up to whole
+        // 32-row MFMA blocks; then tile counts and the largest-work-first order
         std::vector<long> work(g);
         std::vector<int> tiles(g);
         for (int i = 0; i < g; ++i) {
             const int tm = ceil_div(m[i], p->shape.tile_m);
+            int rp = tm ? ceil_div(m[i], tm) : 0;
+            rp = (rp + 31) / 32 * 32;
+            p->tiles_m[i] = tm;
+            p->rows_per[i] = rp;
             tiles[i] = tm * ceil_div(n, p->shape.tile_n);
             work[i] = (long)m[i];
         }
@@ -134,7 +143,8 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
         const int mi = plan->m[i];
         GroupArgs& G = args.grp[s];
         G.m = mi;
-        G.tiles_m = (mi + plan->shape.tile_m - 1) / plan->shape.tile_m;
+        G.tiles_m = plan->tiles_m[i];
+        G.rows_per_tile = plan->rows_per[i];
         if (mi > 0) {
             if (!A[i] || !B[i] || !SFA[i] || !SFB[i] || !C[i]) return NVFP4_GG_EINVAL;
             if (!aligned16(A[i]) || !aligned16(B[i]) || !aligned16(SFA[i]) || !aligned16(SFB[i]) || !aligned16(C[i]))

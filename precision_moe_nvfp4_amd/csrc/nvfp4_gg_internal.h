@@ -17,7 +17,9 @@ struct GroupArgs {
     const uint8_t* sfb;  // [n][k/16] E4M3FN
     uint16_t* c;         // [m][n] fp16 bits
     int m;               // rows of this group
-    int tiles_m;         // ceil(m / tile_m)
+    int tiles_m;         // m chunks of this group
+    int rows_per_tile;   // rows of each m chunk (the last may have fewer)
+    int pad_;
 };
 
 // Kernel arguments, passed by value: the whole group table rides in the kernarg segment.
@@ -37,7 +39,7 @@ struct VariantShape {
 };
 
 enum Variant : int {
-    kVariantTiled128 = 0,  // one 128x128 output tile per workgroup, 4 waves
+    kVariantRing = 1,  // (<= 128 rows) x 256 tile, 8 waves, 4-slot direct-to-LDS ring
 };
 
 VariantShape variant_shape(int variant);
