@@ -1,11 +1,18 @@
 // Host side of the NVFP4 grouped GEMM C ABI: validation, planning and launch.
 //
 // Planning follows the host path of custom_kernel on the page "kernelindex submission
-// 503584": groups are ordered by tile work, largest first, and tiles are numbered through
-// the exclusive prefix sum of the per-group tile counts, m tile fastest inside a group.
-// Unlike that page (which re-uploads a pointer table to device memory whenever the
-// pointers change), the whole group table here travels by value in the kernel
-// arguments, so a call needs no device allocation and no host-to-device copy.
+// 503584" in spirit (groups ordered by work, tiles enumerated over per-group tile counts),
+// but the tile list is built here once per shape and balanced across the compute units:
+//   * every group's rows are cut into equal chunks of at most R rows (multiples of 32) and
+//     the columns into 256-wide tiles, for each candidate R in {32, 64, 96, 128};
+//   * a cost model (MFMA cycles plus the dequantisation VALU cycles that the tile height
+//     implies, per SIMD) prices each tile;
+//   * tiles that read the same B columns (same group, same column tile) are kept on one
+//     XCD, XCDs are balanced, and inside an XCD tiles are dealt largest first to the least
+//     loaded workgroup (LPT);
+//   * the candidate R with the smallest estimated makespan wins.
+// The group table travels by value in the kernel arguments on every call; the tile list
+// is uploaded to device memory once, when the plan is built.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -27,13 +34,17 @@ struct nvfp4_gg_plan_s {
     int num_cus;
     int variant;
     VariantShape shape;
+    int chunk_rows;              // chosen maximum rows per tile
     int total_tiles;
     int grid;
+    double est_cycles;           // estimated makespan of the tile schedule
     std::vector<int> m;          // caller order
-    std::vector<int> tiles_m;    // m chunks per group, caller order
-    std::vector<int> rows_per;   // rows per m chunk, caller order
     std::vector<int> order;      // order[p] = caller group at schedule position p
-    std::vector<int> tile_begin; // size g + 1, schedule order
+    std::vector<int> tile_begin; // per-group tile prefix in schedule order (informational)
+    std::vector<TileDesc> tiles; // tiles grouped by workgroup (group = schedule position)
+    std::vector<int> wg_begin;   // size grid + 1
+    TileDesc* d_tiles = nullptr;
+    int* d_wg_begin = nullptr;
 };
 
 namespace {
@@ -41,12 +52,97 @@ namespace {
 constexpr uint32_t kPlanMagic = 0x4E564634u;  // "NVF4"
 constexpr int kMaxRows = 1 << 20;
 constexpr int kNominalCUs = 256;               // MI355X
+constexpr int kXcds = 8;                       // workgroup b runs on XCD b % 8
+constexpr int kTileCols = 256;
+constexpr int kStepK = 64;
 
 bool plan_ok(const nvfp4_gg_plan_s* p) { return p != nullptr && p->magic == kPlanMagic; }
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Estimated cycles of one tile on one CU.  Per compute step of 64 K, per SIMD (2 waves):
+// 8 * rpad/32 MFMAs 32x32x16 f16 at ~38 cycles each, and ~2.8 cycles for every VALU
+// instruction beside them (B dequantisation and scale conversion ~56 per wave, A
+// dequantisation ~12 per 64 tile rows, measured on MI355X); the operand bytes of a step,
+// (256 + rows) rows x 36 B, arrive at ~21 B per cycle per CU from L2.  Loads overlap the
+// compute; the first superstep's loads and the epilogue do not.
+double tile_cycles(int rows, int k)
+{
+    const int rpad = (rows + 31) & ~31;
+    const int steps = k / kStepK;
+    const double mfma = 8.0 * (rpad / 32) * 38.0;
+    const double valu = (2.0 * 56.0 + 12.0 * ((rpad + 63) / 64)) * 2.8;
+    const double load = (256.0 + rpad) * 36.0 / 21.0;
+    return steps * std::max(mfma + valu, load) + 4.0 * load + 4000.0;
+}
+
+struct Schedule {
+    int chunk_rows = 0;
+    double makespan = 0;
+    std::vector<std::vector<TileDesc>> per_wg;
+};
+
+// Build and balance the tile list for chunk height R (group indices are schedule positions).
+Schedule build_schedule(int R, const std::vector<int>& m_sched, int n, int k, int num_wgs)
+{
+    Schedule S;
+    S.chunk_rows = R;
+    S.per_wg.assign(num_wgs, {});
+    const int ntiles_n = ceil_div(n, kTileCols);
+    struct Cls {
+        double cost;
+        std::vector<std::pair<double, TileDesc>> tiles;
+    };
+    std::vector<Cls> classes;
+    for (int gi = 0; gi < (int)m_sched.size(); ++gi) {
+        const int mi = m_sched[gi];
+        if (mi <= 0) continue;
+        const int chunks = ceil_div(mi, R);
+        const int rp = (ceil_div(mi, chunks) + 31) / 32 * 32;
+        for (int tn = 0; tn < ntiles_n; ++tn) {
+            Cls c{0.0, {}};
+            for (int row0 = 0; row0 < mi; row0 += rp) {
+                const int rows = std::min(rp, mi - row0);
+                const double cost = tile_cycles(rows, k);
+                c.tiles.push_back({cost, TileDesc{gi, row0, rows, tn * kTileCols}});
+                c.cost += cost;
+            }
+            classes.push_back(std::move(c));
+        }
+    }
+    // classes (tiles sharing B columns) to XCDs, largest first, least-loaded XCD
+    const int xcds = std::min(kXcds, num_wgs);
+    std::vector<int> order(classes.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return classes[a].cost > classes[b].cost; });
+    std::vector<double> xload(xcds, 0.0);
+    std::vector<std::vector<std::pair<double, TileDesc>>> xtiles(xcds);
+    for (int ci : order) {
+        const int x = (int)(std::min_element(xload.begin(), xload.end()) - xload.begin());
+        xload[x] += classes[ci].cost;
+        for (auto& t : classes[ci].tiles) xtiles[x].push_back(t);
+    }
+    // inside an XCD: LPT over its workgroups (b = x + xcds * slot); stable order keeps the
+    // tiles of one class next to each other, so they tend to run in the same round
+    std::vector<double> wload(num_wgs, 0.0);
+    for (int x = 0; x < xcds; ++x) {
+        auto& v = xtiles[x];
+        std::stable_sort(v.begin(), v.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
+        std::vector<int> wgs;
+        for (int b = x; b < num_wgs; b += xcds) wgs.push_back(b);
+        for (auto& t : v) {
+            int best = wgs[0];
+            for (int b : wgs)
+                if (wload[b] < wload[best]) best = b;
+            wload[best] += t.first;
+            S.per_wg[best].push_back(t.second);
+        }
+    }
+    S.makespan = num_wgs ? *std::max_element(wload.begin(), wload.end()) : 0.0;
+    return S;
+}
 
 }  // namespace
 
@@ -56,11 +152,19 @@ extern "C" const char* nvfp4_gg_status_string(nvfp4_gg_status_t s)
     case NVFP4_GG_OK: return "success";
     case NVFP4_GG_EINVAL: return "invalid argument";
     case NVFP4_GG_EALIGN: return "device pointer not 16-byte aligned";
-    case NVFP4_GG_ENOMEM: return "host allocation failed";
+    case NVFP4_GG_ENOMEM: return "host or device allocation failed";
     case NVFP4_GG_EHIP: return "HIP runtime error";
     case NVFP4_GG_EUNSUPPORTED: return "unsupported device or configuration";
     }
     return "unknown status";
+}
+
+static void free_device(nvfp4_gg_plan_s* p)
+{
+    if (p->d_tiles) (void)hipFree(p->d_tiles);
+    if (p->d_wg_begin) (void)hipFree(p->d_wg_begin);
+    p->d_tiles = nullptr;
+    p->d_wg_begin = nullptr;
 }
 
 extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k, int device)
@@ -91,35 +195,73 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const in
         p->k = k;
         p->device = device;
         p->num_cus = num_cus;
-        p->variant = kVariantRing;
+        p->variant = kVariantPersistent;
         p->shape = variant_shape(p->variant);
         p->m.assign(m, m + g);
-        p->tiles_m.assign(g, 0);
-        p->rows_per.assign(g, 0);
 
-        // m chunks: as few as the tile height allows, equal sizes rounded up to whole
-        // 32-row MFMA blocks; then tile counts and the largest-work-first order
-        std::vector<long> work(g);
-        std::vector<int> tiles(g);
-        for (int i = 0; i < g; ++i) {
-            const int tm = ceil_div(m[i], p->shape.tile_m);
-            int rp = tm ? ceil_div(m[i], tm) : 0;
-            rp = (rp + 31) / 32 * 32;
-            p->tiles_m[i] = tm;
-            p->rows_per[i] = rp;
-            tiles[i] = tm * ceil_div(n, p->shape.tile_n);
-            work[i] = (long)m[i];
-        }
+        // schedule order of the groups: largest first (stable for ties)
         p->order.resize(g);
         std::iota(p->order.begin(), p->order.end(), 0);
-        std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) { return work[a] > work[b]; });
+        std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) { return m[a] > m[b]; });
+        std::vector<int> m_sched(g);
+        for (int s = 0; s < g; ++s) m_sched[s] = m[p->order[s]];
+
+        // pick the chunk height with the smallest estimated makespan
+        Schedule best;
+        bool have = false;
+        for (int R : {128, 96, 64, 32}) {
+            Schedule S = build_schedule(R, m_sched, n, k, num_cus);
+            if (!have || S.makespan < best.makespan * 0.999) {
+                best = std::move(S);
+                have = true;
+            }
+        }
+        p->chunk_rows = best.chunk_rows;
+        p->est_cycles = best.makespan;
+
+        // flatten: workgroup b's tiles, largest first; grid ends at the last busy workgroup
+        int last = -1;
+        for (int b = 0; b < num_cus; ++b)
+            if (!best.per_wg[b].empty()) last = b;
+        p->grid = last + 1;
+        p->wg_begin.assign(p->grid + 1, 0);
+        for (int b = 0; b < p->grid; ++b) {
+            for (const auto& t : best.per_wg[b]) p->tiles.push_back(t);
+            p->wg_begin[b + 1] = (int)p->tiles.size();
+        }
+        p->total_tiles = (int)p->tiles.size();
+
+        // informational per-group tile prefix (schedule order)
         p->tile_begin.assign(g + 1, 0);
-        for (int s = 0; s < g; ++s) p->tile_begin[s + 1] = p->tile_begin[s] + tiles[p->order[s]];
-        p->total_tiles = p->tile_begin[g];
-        p->grid = p->total_tiles;
+        const int ntn = ceil_div(n, kTileCols);
+        for (int s = 0; s < g; ++s) {
+            const int chunks = m_sched[s] ? ceil_div(m_sched[s], p->chunk_rows) : 0;
+            p->tile_begin[s + 1] = p->tile_begin[s] + chunks * ntn;
+        }
     } catch (...) {
         delete p;
         return NVFP4_GG_ENOMEM;
+    }
+
+    if (device != NVFP4_GG_DEVICE_NONE && p->total_tiles > 0) {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) {
+            delete p;
+            return NVFP4_GG_EHIP;
+        }
+        bool ok = hipMalloc(reinterpret_cast<void**>(&p->d_tiles), sizeof(TileDesc) * p->tiles.size()) == hipSuccess &&
+                  hipMalloc(reinterpret_cast<void**>(&p->d_wg_begin), sizeof(int) * p->wg_begin.size()) == hipSuccess;
+        ok = ok &&
+             hipMemcpy(p->d_tiles, p->tiles.data(), sizeof(TileDesc) * p->tiles.size(), hipMemcpyHostToDevice) ==
+                 hipSuccess &&
+             hipMemcpy(p->d_wg_begin, p->wg_begin.data(), sizeof(int) * p->wg_begin.size(), hipMemcpyHostToDevice) ==
+                 hipSuccess;
+        (void)hipSetDevice(prev);
+        if (!ok) {
+            free_device(p);
+            delete p;
+            return NVFP4_GG_ENOMEM;
+        }
     }
     *out = p;
     return NVFP4_GG_OK;
@@ -137,14 +279,12 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
     args.g = plan->g;
     args.n = plan->n;
     args.k = plan->k;
-    args.total_tiles = plan->total_tiles;
+    args.ntiles = plan->total_tiles;
     for (int s = 0; s < plan->g; ++s) {
         const int i = plan->order[s];
         const int mi = plan->m[i];
         GroupArgs& G = args.grp[s];
         G.m = mi;
-        G.tiles_m = plan->tiles_m[i];
-        G.rows_per_tile = plan->rows_per[i];
         if (mi > 0) {
             if (!A[i] || !B[i] || !SFA[i] || !SFB[i] || !C[i]) return NVFP4_GG_EINVAL;
             if (!aligned16(A[i]) || !aligned16(B[i]) || !aligned16(SFA[i]) || !aligned16(SFB[i]) || !aligned16(C[i]))
@@ -156,8 +296,6 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
             G.c = static_cast<uint16_t*>(C[i]);
         }
     }
-    for (int s = 0; s <= plan->g; ++s) args.tile_begin[s] = plan->tile_begin[s];
-    args.tile_begin[plan->g + 1] = plan->total_tiles;
 
     if (plan->device == NVFP4_GG_DEVICE_NONE) return NVFP4_GG_EUNSUPPORTED;
     int cur = -1;
@@ -165,6 +303,8 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
     if (cur != plan->device) return NVFP4_GG_EINVAL;
     if (plan->total_tiles == 0) return NVFP4_GG_OK;
 
+    args.tiles = plan->d_tiles;
+    args.wg_begin = plan->d_wg_begin;
     if (launch_variant(plan->variant, args, plan->grid, stream) != hipSuccess) return NVFP4_GG_EHIP;
     return NVFP4_GG_OK;
 }
@@ -178,8 +318,8 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_p
     info->k = plan->k;
     info->device = plan->device;
     info->num_cus = plan->num_cus;
-    info->tile_m = plan->shape.tile_m;
-    info->tile_n = plan->shape.tile_n;
+    info->tile_m = plan->chunk_rows;
+    info->tile_n = kTileCols;
     info->total_tiles = plan->total_tiles;
     info->grid = plan->grid;
     info->block = plan->shape.block;
@@ -194,5 +334,6 @@ extern "C" void nvfp4_gg_destroy(nvfp4_gg_plan_t plan)
 {
     if (!plan_ok(plan)) return;
     plan->magic = 0;
+    free_device(plan);
     delete plan;
 }

@@ -17,18 +17,27 @@ struct GroupArgs {
     const uint8_t* sfb;  // [n][k/16] E4M3FN
     uint16_t* c;         // [m][n] fp16 bits
     int m;               // rows of this group
-    int tiles_m;         // m chunks of this group
-    int rows_per_tile;   // rows of each m chunk (the last may have fewer)
     int pad_;
 };
 
-// Kernel arguments, passed by value: the whole group table rides in the kernarg segment.
+// One output tile: rows [row0, row0 + rows) of group `group` (schedule index), columns
+// [col0, col0 + 256).
+struct TileDesc {
+    int group;
+    int row0;
+    int rows;
+    int col0;
+};
+
+// Kernel arguments, passed by value: the whole group table rides in the kernarg segment;
+// the tile list (built once by the planner) lives in device memory owned by the plan.
 struct KernArgs {
     int g;
     int n;
     int k;
-    int total_tiles;
-    int tile_begin[NVFP4_GG_MAX_GROUPS + 2];  // exclusive prefix of tiles, schedule order
+    int ntiles;
+    const TileDesc* tiles;  // tiles in processing order, grouped by workgroup
+    const int* wg_begin;    // workgroup b processes tiles[wg_begin[b] .. wg_begin[b+1])
     GroupArgs grp[NVFP4_GG_MAX_GROUPS];
 };
 static_assert(sizeof(KernArgs) <= 4096, "kernel arguments must fit the 4 KiB kernarg segment");
@@ -39,7 +48,7 @@ struct VariantShape {
 };
 
 enum Variant : int {
-    kVariantRing = 1,  // (<= 128 rows) x 256 tile, 8 waves, 4-slot direct-to-LDS ring
+    kVariantPersistent = 2,  // persistent 8-wave workgroups over a planned tile list
 };
 
 VariantShape variant_shape(int variant);
