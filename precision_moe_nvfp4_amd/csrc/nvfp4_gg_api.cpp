@@ -4,7 +4,7 @@
 // 503584" in spirit (groups ordered by work, tiles enumerated over per-group tile counts),
 // but the tile list is built here once per shape and balanced across the compute units:
 //   * every group's rows are cut into equal chunks of at most R rows (multiples of 32) and
-//     the columns into 256-wide tiles, for each candidate R in {32, 64, 96, 128};
+//     the columns into 128-wide tiles, for each candidate R in {32, 64, 96, 128};
 //   * a cost model (MFMA cycles plus the dequantisation VALU cycles that the tile height
 //     implies, per SIMD) prices each tile;
 //   * tiles that read the same B columns (same group, same column tile) are kept on one
@@ -53,7 +53,7 @@ constexpr uint32_t kPlanMagic = 0x4E564634u;  // "NVF4"
 constexpr int kMaxRows = 1 << 20;
 constexpr int kNominalCUs = 256;               // MI355X
 constexpr int kXcds = 8;                       // workgroup b runs on XCD b % 8
-constexpr int kTileCols = 256;
+constexpr int kTileCols = 128;
 constexpr int kStepK = 64;
 
 bool plan_ok(const nvfp4_gg_plan_s* p) { return p != nullptr && p->magic == kPlanMagic; }
@@ -62,20 +62,21 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Estimated cycles of one tile on one CU.  Per compute step of 64 K, per SIMD (2 waves):
-// 8 * rpad/32 MFMAs 32x32x16 f16 at ~38 cycles each, and ~2.8 cycles for every VALU
-// instruction beside them (B dequantisation and scale conversion ~56 per wave, A
-// dequantisation ~12 per 64 tile rows, measured on MI355X); the operand bytes of a step,
-// (256 + rows) rows x 36 B, arrive at ~21 B per cycle per CU from L2.  Loads overlap the
-// compute; the first superstep's loads and the epilogue do not.
+// Estimated cycles of one tile on one CU, per compute step of 64 K (measured on MI355X):
+//   * MFMA: per SIMD 4 * rpad/32 MFMAs 32x32x16 f16 at ~35 cycles;
+//   * VALU: per SIMD ~2 x 26 instructions for B plus 18 per 64 tile rows for A, at ~4.6
+//     cycles (the conversions are not full rate); it overlaps the MFMAs;
+//   * operand bytes: (128 + rows) rows x 36 B arrive at ~21 B per cycle per CU from L2.
+// The slowest of the three sets the step; the first superstep's loads and the epilogue
+// are not overlapped.
 double tile_cycles(int rows, int k)
 {
     const int rpad = (rows + 31) & ~31;
     const int steps = k / kStepK;
-    const double mfma = 8.0 * (rpad / 32) * 38.0;
-    const double valu = (2.0 * 56.0 + 12.0 * ((rpad + 63) / 64)) * 2.8;
-    const double load = (256.0 + rpad) * 36.0 / 21.0;
-    return steps * std::max(mfma + valu, load) + 4.0 * load + 4000.0;
+    const double mfma = 4.0 * (rpad / 32) * 35.0;
+    const double valu = (2.0 * 26.0 + 18.0 * ((rpad + 63) / 64)) * 4.6;
+    const double load = (kTileCols + rpad) * 36.0 / 21.0;
+    return steps * std::max(std::max(mfma, valu), load) + 4.0 * load + 3000.0;
 }
 
 struct Schedule {

@@ -12,20 +12,25 @@
 // number, and the contraction runs on the fp16 MFMA with fp32 sums.
 //
 // Structure: a persistent grid (one workgroup of 8 waves, 2 per SIMD, per CU) walks a tile
-// list built by the host planner.  A tile is up to 256 rows of one group x 256 columns;
-// wave w owns columns 64 (w & 3) .. +64 and up to 128 rows, so each dequantised B fragment
-// feeds up to 4 MFMAs:
-//   * An LDS ring receives, per K step of 64, the raw bytes of the step (B rows, A rows
-//     and their scales) straight from HBM through direct-to-LDS loads (no VGPR staging).
-//     Its depth follows the tile height (4 slots at 256 rows, 14 at 32 rows), so tiles
-//     with little MFMA work per step keep more steps in flight.
+// list built by the host planner.  A tile is up to 128 rows of one group x 128 columns.
+// Wave w owns the 32 columns 32 (w & 3) .. +32 and all tile rows; the waves w and w + 4
+// split every K step between them.  So each dequantised B fragment feeds one MFMA per 32
+// tile rows, and each A fragment read from LDS feeds one MFMA:
+//   * An LDS ring receives, per superstep of K = 256, the raw bytes of the superstep (B
+//     rows, A rows and their scales) straight from HBM through direct-to-LDS loads (no
+//     VGPR staging), one whole 128-byte line per row and load instruction; 3 or 4
+//     supersteps are in flight, as the tile height allows.
 //   * B (the large operand) is dequantised in registers right before its MFMAs.
-//   * A (shared by the waves) is dequantised once per workgroup into an fp16 LDS buffer,
-//     one step ahead, and read back as MFMA fragments.
+//   * A (shared by the waves) is dequantised once per workgroup into an fp16 LDS buffer
+//     holding one superstep, by all 8 waves in a short phase between supersteps, and read
+//     back as MFMA fragments.
+//   * The 4 compute steps (K = 64) of a superstep run without barriers, so every wave
+//     overlaps its LDS reads, B dequantisation and MFMAs across steps.
 //   * v_mfma_f32_32x32x16_f16 takes the B fragment as its M-side operand, so each lane
 //     ends up holding runs of 4 consecutive C columns (8-byte fp16 stores).
-// K is permuted inside each step, identically for A and B (the dot product is unchanged):
-// MFMA sub-step t takes, in lane half h, the 8 K values starting at 32h + 8t.
+// K is permuted inside each compute step, identically for A and B (the dot product is
+// unchanged): lane half h, wave pair x and sub-step i take the 8 K values starting at
+// 32h + 16x + 8i.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,27 +48,19 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 // Exact dequantisation helpers
 // ---------------------------------------------------------------------------------------
 
-__device__ __forceinline__ h2_t splat2(_Float16 s)
-{
-    h2_t r;
-    r.x = s;
-    r.y = s;
-    return r;
-}
-
-// E4M3FN byte SEL of x -> fp16 pair (hardware OCP E4M3 decode to fp32, exact; the value
-// is a normal fp16 number or zero, so the conversion to fp16 is exact too).
-template <int SEL>
-__device__ __forceinline__ h2_t scale2(uint32_t x)
-{
-    return splat2((_Float16)__builtin_amdgcn_cvt_f32_fp8((int)x, SEL));
-}
-
 // fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 under the default mode).
 __device__ __forceinline__ uint16_t f16_bits_rne(float f)
 {
     const _Float16 h = (_Float16)f;
     return __builtin_bit_cast(uint16_t, h);
+}
+
+// E4M3FN byte 0 of x -> the fp16 pair (s, s).  The hardware OCP E4M3 conversion with
+// scale 1.0 is exact (every E4M3 value is an fp16 number).
+__device__ __forceinline__ h2_t scale_pair(uint32_t x)
+{
+    const h2_t s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+    return h2_t{s.x, s.x};
 }
 
 // 8 E2M1 codes (nibble i = element i, i.e. low nibble = even K) times one fp16 scale ->
@@ -85,66 +82,73 @@ __device__ __forceinline__ u4_t dequant8(uint32_t x, h2_t s)
 // ---------------------------------------------------------------------------------------
 namespace pk {
 constexpr int THREADS = 512;         // 8 waves, 2 per SIMD
-constexpr int BN = 256;              // tile columns: wave w owns columns 64 (w & 3) .. +64
+constexpr int BN = 128;              // tile columns: wave w owns columns 32 (w & 3) .. +32
 constexpr int RMAX = 128;            // tile rows (multiple of 32)
 constexpr int BK = 64;               // K per compute step (4 MFMA sub-steps of 16)
 constexpr int SK = 256;              // K per load superstep
 constexpr int SUB = SK / BK;         // compute steps per superstep
 constexpr int ROWB = SK / 2;         // code bytes per row and superstep: one 128-byte line
 constexpr int SCB = SK / 16;         // scale bytes per row and superstep
+constexpr int MAX_SLOTS = 4;
 constexpr int LDS_BYTES = 160 * 1024;
 // LDS layout of a tile with rpad rows (all offsets multiples of 16 bytes):
-//   [0, 2 * rpad * A_ROW)      fp16 A of two compute steps (double buffer)
+//   [0, rpad * A_ROW)          fp16 A of one superstep
 //   then ring_slots(rpad) slots of slot_bytes(rpad), each holding the raw bytes of one
 //   superstep:
-//     B codes   256 rows x 128 B   at 0            (16-byte chunk c of row r at c ^ (r & 7))
-//     B scales  256 rows x 16 B    at B_SCALES_AT
+//     B codes   128 rows x 128 B   at 0            (16-byte chunk c of row r at c ^ (r & 7))
+//     B scales  128 rows x 16 B    at B_SCALES_AT
 //     A codes   rpad rows x 128 B  at A_CODES_AT   (same chunk swizzle)
 //     A scales  rpad rows x 16 B   at A_CODES_AT + 128 rpad
 // Whole 128-byte lines per row and load instruction: a wave's 16-byte lanes cover 8 rows
 // per instruction instead of 32, which is what lets a CU pull shared operand rows out of
 // L2 at ~3x the rate of 32-byte row pieces.
-constexpr int A_ROW = BK * 2 + 16;                    // 144 B per fp16 row (spreads banks)
-constexpr int B_SCALES_AT = BN * ROWB;                // 32768
-constexpr int A_CODES_AT = B_SCALES_AT + BN * SCB;    // 36864
+constexpr int A_ROW = SK * 2 + 16;                    // 528 B per fp16 row (spreads banks)
+constexpr int B_SCALES_AT = BN * ROWB;                // 16384
+constexpr int A_CODES_AT = B_SCALES_AT + BN * SCB;    // 18432
 __host__ __device__ constexpr int slot_bytes(int rpad) { return A_CODES_AT + rpad * (ROWB + SCB); }
-__host__ __device__ constexpr int ring_base(int rpad) { return 2 * rpad * A_ROW; }
+__host__ __device__ constexpr int ring_base(int rpad) { return rpad * A_ROW; }
 __host__ __device__ constexpr int ring_slots(int rpad)
 {
-    return (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad) > 3 ? 3 : (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad);
+    return (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad) > MAX_SLOTS
+               ? MAX_SLOTS
+               : (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad);
 }
+// pair reduction area: per wave, for each 32-row block, two u4 per lane
+constexpr int RED_WAVE = (RMAX / 32) * 2 * 64 * 16;
 static_assert(ring_slots(RMAX) >= 2, "the tallest tile needs at least 2 ring slots");
-static_assert(8 * 4 * 4 * 1024 <= LDS_BYTES, "pair-reduction area must fit in LDS");
+static_assert(8 * RED_WAVE <= LDS_BYTES, "pair-reduction area must fit in LDS");
 }  // namespace pk
 
-// Wave roles: both waves of a pair (x = w >> 2) take all tile rows and split the MFMA
-// sub-steps (x takes sub-steps x and x + 2 of each compute step); the two partial sums
-// are added through LDS at the end.
+// ---------------------------------------------------------------------------------------
+// Loads
+// ---------------------------------------------------------------------------------------
 
-// Per-wave direct-to-LDS loads of one superstep.  Wave w fetches B rows 32w .. +32 (four
-// instructions of 8 rows x 128 B) and their scales (lanes < 32, 16 B each); the A rows are
-// dealt round-robin: code instruction i (rows 8i .. +8) to wave i % 8, scale instruction q
-// (rows 32q .. +32) to wave 7 - q.
+// Per-wave direct-to-LDS loads of one superstep.  B code instruction i (rows 8i .. +8,
+// i < 16) goes to wave i % 8, B scale instruction q (rows 32q .. +32, lanes < 32) to
+// wave q; A code instruction a (rows 8a .. +8) to wave (a + 4) % 8, A scale instruction q
+// to wave 7 - q.
 struct SuperLoads {
-    const uint8_t* b[4];  // B codes of this lane, superstep 0
+    const uint8_t* b[2];  // B codes of this lane, superstep 0
     const uint8_t* sb;    // B scales of this lane (lanes < 32)
-    const uint8_t* a[2];  // A codes of this lane, for the wave's A code instructions
+    const uint8_t* a[2];  // A codes of this lane
     const uint8_t* sa;    // A scales of this lane (lanes < 32)
+    int b_dst[2];         // LDS offsets (inside a slot) of the B code instructions
+    int sb_dst;
+    int a_dst[2];
+    int sa_dst;
+    int nsb;              // B scale instructions of this wave (0 or 1)
     int na;               // A code instructions of this wave (0 .. 2)
     int nsa;              // A scale instructions of this wave (0 or 1)
-    int a_dst[2];         // LDS offsets (inside a slot) of the A code instructions
-    int sa_dst;           // LDS offset (inside a slot) of the A scale instruction
     int ops;              // loads per superstep issued by this wave
 };
 
-__device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, const SuperLoads& L, int wave, int lane)
+__device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, const SuperLoads& L, int lane)
 {
     using namespace pk;
     const long kb = (long)t * ROWB, ks = (long)t * SCB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(L.b[i] + kb, slot_base + (32 * wave + 8 * i) * ROWB, 16, 0, 0);
-    if (lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + B_SCALES_AT + 32 * wave * SCB, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(L.b[0] + kb, slot_base + L.b_dst[0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(L.b[1] + kb, slot_base + L.b_dst[1], 16, 0, 0);
+    if (L.nsb > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 16, 0, 0);
     if (L.na > 0) __builtin_amdgcn_global_load_lds(L.a[0] + kb, slot_base + L.a_dst[0], 16, 0, 0);
     if (L.na > 1) __builtin_amdgcn_global_load_lds(L.a[1] + kb, slot_base + L.a_dst[1], 16, 0, 0);
     if (L.nsa > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 16, 0, 0);
@@ -177,197 +181,167 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Dequantise the A bytes of compute step U of the superstep held at `slot_base` into the
-// fp16 buffer `dst` (natural K order, A_ROW-byte rows).  Waves 0..3 (one per SIMD) take
-// rpad pieces each; piece id covers row id / 4, K values 16 (id % 4) .. +16 of the step
-// (8 code bytes, one scale byte).  Rows in [rows, rpad) become zeros.
-template <int U>
-__device__ __forceinline__ void pk_dequant_a(const uint8_t* slot_base, uint8_t* dst, int rows, int rpad, int wave,
-                                             int lane)
+// ---------------------------------------------------------------------------------------
+// A operand: raw bytes -> fp16 LDS buffer
+// ---------------------------------------------------------------------------------------
+
+// Dequantise the A bytes of the superstep held at `slot_base` into the fp16 buffer (natural
+// K order, A_ROW-byte rows), all 8 waves together.  Piece id = tid + 512 i covers row
+// id / 16, K values 16 (id % 16) .. +16 (8 code bytes, one scale byte).  Rows in
+// [rows, rpad) get scale 0, so they dequantise to zeros.
+template <int NRB>
+__device__ __forceinline__ void pk_dequant_a(const uint8_t* slot_base, uint8_t* a16, int rows, int tid)
 {
     using namespace pk;
-    if (wave >= 4) return;
+    constexpr int rpad = 32 * NRB;
     const uint8_t* codes = slot_base + A_CODES_AT;
     const uint8_t* scales = codes + rpad * ROWB;
+    u2_t q[NRB];
+    uint32_t sc[NRB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int id = wave * rpad + lane + 64 * i;
-        if (lane + 64 * i >= rpad) continue;
-        const int r = id >> 2, p = id & 3;
-        u4_t* d = reinterpret_cast<u4_t*>(dst + r * A_ROW + 32 * p);
-        if (r < rows) {
-            const int chunk = 2 * U + (p >> 1);
-            const u2_t q = *reinterpret_cast<const u2_t*>(codes + r * ROWB + 16 * (chunk ^ (r & 7)) + 8 * (p & 1));
-            const h2_t sc = scale2<0>(scales[r * SCB + 4 * U + p]);
-            d[0] = dequant8(q.x, sc);
-            d[1] = dequant8(q.y, sc);
-        } else {
-            const u4_t z = {0u, 0u, 0u, 0u};
-            d[0] = z;
-            d[1] = z;
-        }
+    for (int i = 0; i < NRB; ++i) {
+        const int id = tid + THREADS * i;
+        const int r = id >> 4, p = id & 15;
+        q[i] = *reinterpret_cast<const u2_t*>(codes + r * ROWB + 16 * ((p >> 1) ^ (r & 7)) + 8 * (p & 1));
+        const uint32_t s8 = scales[r * SCB + p];
+        sc[i] = r < rows ? s8 : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+        const int id = tid + THREADS * i;
+        const int r = id >> 4, p = id & 15;
+        u4_t* d = reinterpret_cast<u4_t*>(a16 + r * A_ROW + 32 * p);
+        const h2_t s2 = scale_pair(sc[i]);
+        d[0] = dequant8(q[i].x, s2);
+        d[1] = dequant8(q[i].y, s2);
     }
 }
 
-// One wave's B bytes of a step: per 32-column block cb, the lane's 16 bytes of row
-// 64 wn + 32 cb + j (K values 32h .. 32h+31) and the two scale bytes of those values.
-struct PkB {
-    u4_t q[2];
-    uint32_t s[2];
+// ---------------------------------------------------------------------------------------
+// B operand: raw bytes -> registers
+// ---------------------------------------------------------------------------------------
+
+// One wave's raw B operand of a compute step: the lane's 8 code bytes of row 32 cb + j for
+// its two sub-steps (K values 32h + 16x .. +16 of the step, one 16-value scale block) and
+// the row's scale word of the step (4 bytes, one per 16 K values).
+struct BRaw {
+    u2_t q;
+    uint32_t w;
 };
 
-// B codes of compute step U: lane (j, h) reads chunk 2U + h of its row.  The row's 16
-// scale bytes of the superstep are read once per superstep (pk_read_bs).
 template <int U>
-__device__ __forceinline__ void pk_read_b(PkB& r, const uint8_t* slot_base, const u4_t (&bs)[2], int wn, int lane)
+__device__ __forceinline__ void pk_read_b(BRaw& r, const uint8_t* slot_base, int cb, int lane, int x)
 {
     using namespace pk;
     const int j = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const int row = 64 * wn + 32 * cb + j;
-        r.q[cb] = *reinterpret_cast<const u4_t*>(slot_base + row * ROWB + 16 * ((2 * U + h) ^ (row & 7)));
-        const uint32_t w = bs[cb][U];
-        r.s[cb] = h ? (w >> 16) : w;
-    }
+    const int row = 32 * cb + j;
+    r.q = *reinterpret_cast<const u2_t*>(slot_base + row * ROWB + 16 * ((2 * U + h) ^ (row & 7)) + 8 * x);
+    r.w = *reinterpret_cast<const uint32_t*>(slot_base + B_SCALES_AT + row * SCB + 4 * U);
 }
 
-__device__ __forceinline__ void pk_read_bs(u4_t (&bs)[2], const uint8_t* slot_base, int wn, int lane)
+// Dequantise both sub-steps of the raw B operand.  `bsel` is a byte selector that copies
+// this lane's scale byte (byte 2h + x of the word) into bytes 0 and 1.
+__device__ __forceinline__ void pk_dequant_b(h8_t (&bf)[2], const BRaw& r, uint32_t bsel)
+{
+    const uint32_t pair = __builtin_amdgcn_perm(0u, r.w, bsel);
+    const h2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false);
+    bf[0] = __builtin_bit_cast(h8_t, dequant8(r.q.x, sc));
+    bf[1] = __builtin_bit_cast(h8_t, dequant8(r.q.y, sc));
+}
+
+// ---------------------------------------------------------------------------------------
+// Compute steps
+// ---------------------------------------------------------------------------------------
+
+// Compute step U of the superstep held at `cur` (A in the fp16 buffer).  On entry `b`
+// holds the raw B operand of step U; for U < 3 it holds that of step U + 1 on exit (read
+// here, ahead of its use, so that the read overlaps this step's work).
+template <int NRB, int U>
+__device__ __forceinline__ void pk_step(f16v_t (&acc)[NRB], BRaw& b, const uint8_t* cur, const uint8_t* arow,
+                                        uint32_t bsel, int cb, int lane, int x)
 {
     using namespace pk;
-    const int j = lane & 31;
+    h8_t af[2][NRB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-        bs[cb] = *reinterpret_cast<const u4_t*>(slot_base + B_SCALES_AT + (64 * wn + 32 * cb + j) * SCB);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            af[i][rb] = *reinterpret_cast<const h8_t*>(arow + rb * 32 * A_ROW + 2 * BK * U + 16 * i);
+    BRaw bn;
+    if constexpr (U + 1 < SUB) pk_read_b<U + 1>(bn, cur, cb, lane, x);
+    h8_t bf[2];
+    pk_dequant_b(bf, b, bsel);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[i], af[i][rb], acc[rb], 0, 0, 0);
+    if constexpr (U + 1 < SUB) b = bn;
 }
 
-// Fragments of MFMA sub-step T (lane half h: K values 32h + 8T ..): B dequantised from the
-// step's bytes (scale byte T/2 of the lane's pair), A read from the fp16 buffer.
-template <int NRB, int T>
-__device__ __forceinline__ void pk_frags(h8_t (&bf)[2], h8_t (&af)[NRB], const PkB& b, const uint8_t* arow)
+// ---------------------------------------------------------------------------------------
+// Epilogue
+// ---------------------------------------------------------------------------------------
+
+// Pair reduction and store.  Lane (j, h) holds, in acc[rb] element 4q + e, the partial sum
+// of C[32 rb + j][32 cb + 8 q + 4 h + e].  Wave pair x keeps the element groups q = 2x,
+// 2x + 1 and hands the other two to its partner (wave w ^ 4) through LDS.
+template <int NRB, int KEEP>
+__device__ __forceinline__ void pk_reduce_store(f16v_t (&acc)[NRB], uint8_t* smem, uint16_t* __restrict__ c, int n,
+                                                int rows, int col, int wave, int lane)
 {
+    using namespace pk;
+    constexpr int GIVE = 1 - KEEP;
+    u4_t* mine = reinterpret_cast<u4_t*>(smem + wave * RED_WAVE);
+    const u4_t* theirs = reinterpret_cast<const u4_t*>(smem + (wave ^ 4) * RED_WAVE);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
-        af[rb] = *reinterpret_cast<const h8_t*>(arow + rb * 32 * pk::A_ROW + 16 * T);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-        bf[cb] = __builtin_bit_cast(h8_t, dequant8(b.q[cb][T], scale2<(T >> 1)>(b.s[cb])));
-}
-
-template <int NRB>
-__device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[NRB][2], const h8_t (&bf)[2], const h8_t (&af)[NRB])
-{
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[0], af[rb], acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[1], af[rb], acc[rb][1], 0, 0, 0);
-    }
-}
-
-// One compute step of this wave's MFMAs: sub-steps x and x + 2.  The fragments of both
-// are prepared before the MFMAs run.
-template <int NRB>
-__device__ __forceinline__ void pk_compute(f16v_t (&acc)[NRB][2], const PkB& b, const uint8_t* arow, int x)
-{
-    h8_t bf[2][2], af[2][NRB];
-    if (x == 0) {
-        pk_frags<NRB, 0>(bf[0], af[0], b, arow);
-        pk_frags<NRB, 2>(bf[1], af[1], b, arow);
-    } else {
-        pk_frags<NRB, 1>(bf[0], af[0], b, arow);
-        pk_frags<NRB, 3>(bf[1], af[1], b, arow);
-    }
-    pk_mfmas<NRB>(acc, bf[0], af[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    pk_mfmas<NRB>(acc, bf[1], af[1]);
-}
-
-// fp32 -> fp16 (round to nearest even) and store of column block CB: lane (j, h) holds
-// C[32 rb + j][colw + 32 CB + 8 q + 4 h + e], e = 0..3, relative to the wave's first row.
-template <int NRB, int CB>
-__device__ __forceinline__ void pk_store_cb(const f16v_t (&acc)[NRB][2], uint16_t* __restrict__ c, int n, int rows,
-                                            int colw, int lane)
-{
+        for (int e = 0; e < 2; ++e) {
+            const int q = 2 * GIVE + e;
+            mine[(rb * 2 + e) * 64 + lane] =
+                u4_t{__float_as_uint(acc[rb][4 * q + 0]), __float_as_uint(acc[rb][4 * q + 1]),
+                     __float_as_uint(acc[rb][4 * q + 2]), __float_as_uint(acc[rb][4 * q + 3])};
+        }
+    barrier_lds();
     const int j = lane & 31, h = lane >> 5;
     const bool vec_ok = (n & 3) == 0;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
         const int r = rb * 32 + j;
-        if (r >= rows) continue;
-        uint16_t* crow = c + (long)r * n;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int col = colw + CB * 32 + q * 8 + h * 4;
-            const uint16_t v0 = f16_bits_rne(acc[rb][CB][4 * q + 0]);
-            const uint16_t v1 = f16_bits_rne(acc[rb][CB][4 * q + 1]);
-            const uint16_t v2 = f16_bits_rne(acc[rb][CB][4 * q + 2]);
-            const uint16_t v3 = f16_bits_rne(acc[rb][CB][4 * q + 3]);
-            if (vec_ok && col + 4 <= n) {
-                *reinterpret_cast<u2_t*>(crow + col) =
+        for (int e = 0; e < 2; ++e) {
+            const int q = 2 * KEEP + e;
+            const u4_t o = theirs[(rb * 2 + e) * 64 + lane];
+            // (element-wise __uint_as_float: __builtin_bit_cast of an ext-vector element
+            // reads element 0 with this compiler)
+            const uint16_t v0 = f16_bits_rne(acc[rb][4 * q + 0] + __uint_as_float(o.x));
+            const uint16_t v1 = f16_bits_rne(acc[rb][4 * q + 1] + __uint_as_float(o.y));
+            const uint16_t v2 = f16_bits_rne(acc[rb][4 * q + 2] + __uint_as_float(o.z));
+            const uint16_t v3 = f16_bits_rne(acc[rb][4 * q + 3] + __uint_as_float(o.w));
+            if (r >= rows) continue;
+            uint16_t* crow = c + (long)r * n;
+            const int cc = col + 8 * q + 4 * h;
+            if (vec_ok && cc + 4 <= n) {
+                *reinterpret_cast<u2_t*>(crow + cc) =
                     u2_t{(uint32_t)v0 | ((uint32_t)v1 << 16), (uint32_t)v2 | ((uint32_t)v3 << 16)};
             } else {
-                if (col + 0 < n) crow[col + 0] = v0;
-                if (col + 1 < n) crow[col + 1] = v1;
-                if (col + 2 < n) crow[col + 2] = v2;
-                if (col + 3 < n) crow[col + 3] = v3;
+                if (cc + 0 < n) crow[cc + 0] = v0;
+                if (cc + 1 < n) crow[cc + 1] = v1;
+                if (cc + 2 < n) crow[cc + 2] = v2;
+                if (cc + 3 < n) crow[cc + 3] = v3;
             }
         }
     }
 }
 
-// K-split pair reduction, column block GIVE handed to the partner and block KEEP kept:
-// write acc[.][GIVE] to this wave's LDS area, wait for the partner, add the partner's
-// contribution to acc[.][KEEP].  Area of wave (wn, x): 16 KiB at (wn * 2 + x) * 16 KiB.
-template <int NRB, int GIVE, int KEEP>
-__device__ __forceinline__ void pk_pair_reduce(f16v_t (&acc)[NRB][2], u4_t* red, int wn, int x, int lane)
-{
-    u4_t* mine = red + (wn * 2 + x) * 1024;
-    const u4_t* theirs = red + (wn * 2 + (1 - x)) * 1024;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            mine[(rb * 4 + e) * 64 + lane] =
-                u4_t{__float_as_uint(acc[rb][GIVE][4 * e + 0]), __float_as_uint(acc[rb][GIVE][4 * e + 1]),
-                     __float_as_uint(acc[rb][GIVE][4 * e + 2]), __float_as_uint(acc[rb][GIVE][4 * e + 3])};
-    barrier_lds();
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const u4_t o = theirs[(rb * 4 + e) * 64 + lane];
-            // (element-wise __uint_as_float: __builtin_bit_cast of an ext-vector element
-            // reads element 0 with this compiler)
-            acc[rb][KEEP][4 * e + 0] += __uint_as_float(o.x);
-            acc[rb][KEEP][4 * e + 1] += __uint_as_float(o.y);
-            acc[rb][KEEP][4 * e + 2] += __uint_as_float(o.z);
-            acc[rb][KEEP][4 * e + 3] += __uint_as_float(o.w);
-        }
-}
+// ---------------------------------------------------------------------------------------
+// Tile
+// ---------------------------------------------------------------------------------------
 
-// Compute step U of superstep t (slot `cur`), then the A dequantisation of the next step
-// (from `cur`, or from `nxt` when U is the last step of the superstep).
-template <int NRB, int U>
-__device__ __forceinline__ void pk_step(f16v_t (&acc)[NRB][2], const uint8_t* cur, const uint8_t* nxt,
-                                        const u4_t (&bs)[2], uint8_t* a16, int s, int steps, int rows, int rpad,
-                                        int wave, int lane)
-{
-    using namespace pk;
-    const int wn = wave & 3, x = wave >> 2;
-    const int j = lane & 31, h = lane >> 5;
-    PkB b;
-    pk_read_b<U>(b, cur, bs, wn, lane);
-    pk_compute<NRB>(acc, b, a16 + (s & 1) * rpad * A_ROW + j * A_ROW + 64 * h, x);
-    if (s + 1 < steps) {
-        uint8_t* dst = a16 + ((s + 1) & 1) * rpad * A_ROW;
-        if constexpr (U + 1 < SUB) pk_dequant_a<U + 1>(cur, dst, rows, rpad, wave, lane);
-        else pk_dequant_a<0>(nxt, dst, rows, rpad, wave, lane);
-    }
-}
-
-// One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 256)).  All
-// 8 waves execute the same sequence of loads, dequantisations and barriers; NRB = rpad / 32
-// only changes this wave's MFMAs and epilogue.
+// One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)).  All
+// 8 waves execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs
+// per B fragment.
 template <int NRB>
 __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_, uint8_t* smem)
 {
@@ -378,9 +352,10 @@ __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row
     const int col0 = __builtin_amdgcn_readfirstlane(col0_);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & 3, x = wave >> 2;
+    const int cb = wave & 3, x = wave >> 2;
+    const int j = lane & 31, h = lane >> 5;
     const int rpad = 32 * NRB;
-    const int steps = k / BK, supers = k / SK;
+    const int supers = k / SK;
     const long qs = k / 2, ss = k / 16;
 
     const int sbytes = slot_bytes(rpad), nslots = ring_slots(rpad);
@@ -394,87 +369,78 @@ __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row
     {
         const int rl = lane >> 3, pos = lane & 7;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 32 * wave + 8 * i + rl;
-            const long brow = min(col0 + r, n - 1);
-            L.b[i] = G.b + brow * qs + 16 * (pos ^ (r & 7));
+        for (int q = 0; q < 2; ++q) {
+            const int i = wave + 8 * q;   // B code instruction
+            const int r = 8 * i + rl;
+            L.b[q] = G.b + (long)min(col0 + r, n - 1) * qs + 16 * (pos ^ (r & 7));
+            L.b_dst[q] = 8 * i * ROWB;
         }
-        L.sb = G.sfb + (long)min(col0 + 32 * wave + (lane & 31), n - 1) * ss;
+        L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
+        L.sb = G.sfb + (long)min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) * ss;
+        L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
         const int na_total = rpad / 8, nsa_total = rpad / 32;
         L.na = 0;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int i = wave + 8 * q;    // A code instruction handled by this wave
-            const int r = 8 * i + rl;
+            const int a = ((wave + 4) & 7) + 8 * q;   // A code instruction
+            const int r = 8 * a + rl;
             L.a[q] = G.a + (long)(row0 + min(r, rows - 1)) * qs + 16 * (pos ^ (r & 7));
-            L.a_dst[q] = A_CODES_AT + 8 * i * ROWB;
-            if (i < na_total) L.na = q + 1;
+            L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
+            if (a < na_total) L.na = q + 1;
         }
-        const int qa = 7 - wave;            // A scale instruction handled by this wave
+        const int qa = 7 - wave;         // A scale instruction
         L.nsa = qa < nsa_total ? 1 : 0;
         L.sa = G.sfa + (long)(row0 + min(32 * qa + (lane & 31), rows - 1)) * ss;
         L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
-        L.ops = 5 + L.na + L.nsa;
+        L.ops = 2 + L.nsb + L.na + L.nsa;
     }
 
-    f16v_t acc[NRB][2];
+    f16v_t acc[NRB];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        acc[rb][0] = f16v_t{};
-        acc[rb][1] = f16v_t{};
-    }
+    for (int rb = 0; rb < NRB; ++rb) acc[rb] = f16v_t{};
 
-    // prologue: supersteps 0 .. nslots-1 in flight; wait for superstep 0; dequantise A of
-    // compute step 0
+    // prologue: supersteps 0 .. nslots-1 in flight; wait for superstep 0; dequantise its A
+    // and read the raw B operand of its first step
     const int first = min(nslots, supers);
-    for (int t = 0; t < first; ++t) pk_issue(ring + t * sbytes, t, L, wave, lane);
+    for (int t = 0; t < first; ++t) pk_issue(ring + t * sbytes, t, L, lane);
     pk_wait_loads((first - 1) * L.ops);
     barrier_lds();
-    pk_dequant_a<0>(ring, a16, rows, rpad, wave, lane);
+    BRaw b;
+    pk_read_b<0>(b, ring, cb, lane, x);
+    pk_dequant_a<NRB>(ring, a16, rows, tid);
     barrier_lds();
 
+    const uint8_t* arow = a16 + j * A_ROW + 64 * h + 32 * x;   // this lane's A fragment row
+    const uint32_t bsel = 0x0c0c0000u | ((uint32_t)(2 * h + x) << 8) | (uint32_t)(2 * h + x);
     int cs = 0;   // slot of superstep t
     for (int t = 0; t < supers; ++t) {
-        // the slot of superstep t - 1 is free since the last barrier: refill it with
-        // superstep t - 1 + nslots
-        if (t > 0 && t - 1 + nslots < supers) {
-            const int fs = (cs == 0) ? nslots - 1 : cs - 1;
-            pk_issue(ring + fs * sbytes, t - 1 + nslots, L, wave, lane);
-        }
-        const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
         const uint8_t* cur = ring + cs * sbytes;
-        const uint8_t* nxt = ring + ns * sbytes;
-        u4_t bs[2];
-        pk_read_bs(bs, cur, wn, lane);
-        const int s0 = SUB * t;
-        pk_step<NRB, 0>(acc, cur, nxt, bs, a16, s0 + 0, steps, rows, rpad, wave, lane);
-        barrier_lds();
-        pk_step<NRB, 1>(acc, cur, nxt, bs, a16, s0 + 1, steps, rows, rpad, wave, lane);
-        barrier_lds();
-        pk_step<NRB, 2>(acc, cur, nxt, bs, a16, s0 + 2, steps, rows, rpad, wave, lane);
-        // superstep t + 1 must have landed before the next step dequantises its A bytes
-        {
+        pk_step<NRB, 0>(acc, b, cur, arow, bsel, cb, lane, x);
+        pk_step<NRB, 1>(acc, b, cur, arow, bsel, cb, lane, x);
+        pk_step<NRB, 2>(acc, b, cur, arow, bsel, cb, lane, x);
+        pk_step<NRB, 3>(acc, b, cur, arow, bsel, cb, lane, x);
+        if (t + 1 < supers) {
+            // superstep t + 1 must have landed; after the barrier nobody reads superstep
+            // t's slot or the fp16 A buffer any more
             const int last = min(supers - 1, t - 1 + nslots);   // last superstep issued
-            const int need = min(supers - 1, t + 1);
-            pk_wait_loads((last - need) * L.ops);
+            pk_wait_loads((last - (t + 1)) * L.ops);
+            barrier_lds();
+            if (t + nslots < supers) pk_issue(ring + cs * sbytes, t + nslots, L, lane);
+            cs = (cs + 1 == nslots) ? 0 : cs + 1;
+            const uint8_t* nxt = ring + cs * sbytes;
+            pk_read_b<0>(b, nxt, cb, lane, x);
+            pk_dequant_a<NRB>(nxt, a16, rows, tid);
+            barrier_lds();
         }
-        barrier_lds();
-        pk_step<NRB, 3>(acc, cur, nxt, bs, a16, s0 + 3, steps, rows, rpad, wave, lane);
-        barrier_lds();
-        cs = ns;
     }
+    // every wave is past its last LDS read of the loop
+    barrier_lds();
 
-    // pair reduction: wave x keeps column block x and hands block 1 - x to its partner
-    const int colw = col0 + 64 * wn;
-    u4_t* red = reinterpret_cast<u4_t*>(smem);
+    // all loads have landed (the last superstep was waited for) and no wave reads the ring
+    // any more: the reduction area may overwrite it
     uint16_t* c = G.c + (long)row0 * n;
-    if (x == 0) {
-        pk_pair_reduce<NRB, 1, 0>(acc, red, wn, x, lane);
-        pk_store_cb<NRB, 0>(acc, c, n, rows, colw, lane);
-    } else {
-        pk_pair_reduce<NRB, 0, 1>(acc, red, wn, x, lane);
-        pk_store_cb<NRB, 1>(acc, c, n, rows, colw, lane);
-    }
+    if (x == 0) pk_reduce_store<NRB, 0>(acc, smem, c, n, rows, col0 + 32 * cb, wave, lane);
+    else pk_reduce_store<NRB, 1>(acc, smem, c, n, rows, col0 + 32 * cb, wave, lane);
     // the next tile's loads reuse the LDS just read
     barrier_lds();
 }
