@@ -4,7 +4,7 @@
 // 503584" in spirit (groups ordered by work, tiles enumerated over per-group tile counts),
 // but the tile list is built here once per shape and balanced across the compute units:
 //   * every group's rows are cut into equal chunks of at most R rows (multiples of 32) and
-//     the columns into 128-wide tiles, for each candidate R in {32, 64, 96, 128};
+//     the columns into 128-wide tiles, for each candidate R in {32, 64, 96};
 //   * a cost model (MFMA cycles plus the dequantisation VALU cycles that the tile height
 //     implies, per SIMD) prices each tile;
 //   * tiles that read the same B columns (same group, same column tile) are kept on one
@@ -210,7 +210,7 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const in
         // pick the chunk height with the smallest estimated makespan
         Schedule best;
         bool have = false;
-        for (int R : {128, 96, 64, 32}) {
+        for (int R : {96, 64, 32}) {
             Schedule S = build_schedule(R, m_sched, n, k, num_cus);
             if (!have || S.makespan < best.makespan * 0.999) {
                 best = std::move(S);

@@ -12,7 +12,7 @@
 // number, and the contraction runs on the fp16 MFMA with fp32 sums.
 //
 // Structure: a persistent grid (one workgroup of 8 waves, 2 per SIMD, per CU) walks a tile
-// list built by the host planner.  A tile is up to 128 rows of one group x 128 columns.
+// list built by the host planner.  A tile is up to 96 rows of one group x 128 columns.
 // Wave w owns the 32 columns 32 (w & 3) .. +32 and all tile rows; the waves w and w + 4
 // split every K step between them.  So each dequantised B fragment feeds one MFMA per 32
 // tile rows, and each A fragment read from LDS feeds one MFMA:
@@ -21,11 +21,11 @@
 //     VGPR staging), one whole 128-byte line per row and load instruction; 3 or 4
 //     supersteps are in flight, as the tile height allows.
 //   * B (the large operand) is dequantised in registers right before its MFMAs.
-//   * A (shared by the waves) is dequantised once per workgroup into an fp16 LDS buffer
-//     holding one superstep, by all 8 waves in a short phase between supersteps, and read
-//     back as MFMA fragments.
-//   * The 4 compute steps (K = 64) of a superstep run without barriers, so every wave
-//     overlaps its LDS reads, B dequantisation and MFMAs across steps.
+//   * A (shared by the waves) is dequantised once per workgroup, by all 8 waves, into a
+//     double-buffered fp16 LDS buffer holding half a superstep (K = 128), one half ahead of
+//     its use, and read back as MFMA fragments.
+//   * The 2 compute steps (K = 64) of a half run without barriers; the dequantisation of
+//     the next half overlaps their MFMAs.
 //   * v_mfma_f32_32x32x16_f16 takes the B fragment as its M-side operand, so each lane
 //     ends up holding runs of 4 consecutive C columns (8-byte fp16 stores).
 // K is permuted inside each compute step, identically for A and B (the dot product is
@@ -83,30 +83,37 @@ __device__ __forceinline__ u4_t dequant8(uint32_t x, h2_t s)
 namespace pk {
 constexpr int THREADS = 512;         // 8 waves, 2 per SIMD
 constexpr int BN = 128;              // tile columns: wave w owns columns 32 (w & 3) .. +32
-constexpr int RMAX = 128;            // tile rows (multiple of 32)
+constexpr int RMAX = 96;             // tile rows (multiple of 32)
 constexpr int BK = 64;               // K per compute step (4 MFMA sub-steps of 16)
 constexpr int SK = 256;              // K per load superstep
-constexpr int SUB = SK / BK;         // compute steps per superstep
+constexpr int HK = SK / 2;           // K per half superstep (one fp16 A buffer)
 constexpr int ROWB = SK / 2;         // code bytes per row and superstep: one 128-byte line
 constexpr int SCB = SK / 16;         // scale bytes per row and superstep
 constexpr int MAX_SLOTS = 4;
 constexpr int LDS_BYTES = 160 * 1024;
 // LDS layout of a tile with rpad rows (all offsets multiples of 16 bytes):
-//   [0, rpad * A_ROW)          fp16 A of one superstep
+//   [0, 2 * rpad * A_ROW)      fp16 A of two half supersteps (double buffer)
 //   then ring_slots(rpad) slots of slot_bytes(rpad), each holding the raw bytes of one
 //   superstep:
-//     B codes   128 rows x 128 B   at 0            (16-byte chunk c of row r at c ^ (r & 7))
+//     B codes   128 rows x 128 B   at 0            (16-byte chunk c of row r at c ^ swz(r))
 //     B scales  128 rows x 16 B    at B_SCALES_AT
 //     A codes   rpad rows x 128 B  at A_CODES_AT   (same chunk swizzle)
 //     A scales  rpad rows x 16 B   at A_CODES_AT + 128 rpad
 // Whole 128-byte lines per row and load instruction: a wave's 16-byte lanes cover 8 rows
 // per instruction instead of 32, which is what lets a CU pull shared operand rows out of
 // L2 at ~3x the rate of 32-byte row pieces.
-constexpr int A_ROW = SK * 2 + 16;                    // 528 B per fp16 row (spreads banks)
+constexpr int A_ROW = HK * 2 + 16;                    // 272 B per fp16 row (spreads banks)
+// Chunk swizzle of the raw rows: the 3-bit reversal of (r >> 1) & 7.  Reads of one chunk
+// from 16 consecutive rows (16 bytes per lane) and reads of half a row from 4 consecutive
+// rows (4 bytes per lane) then hit 64 distinct banks.
+__host__ __device__ constexpr int swz(int r)
+{
+    return (((r >> 1) & 1) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1);
+}
 constexpr int B_SCALES_AT = BN * ROWB;                // 16384
 constexpr int A_CODES_AT = B_SCALES_AT + BN * SCB;    // 18432
 __host__ __device__ constexpr int slot_bytes(int rpad) { return A_CODES_AT + rpad * (ROWB + SCB); }
-__host__ __device__ constexpr int ring_base(int rpad) { return rpad * A_ROW; }
+__host__ __device__ constexpr int ring_base(int rpad) { return 2 * rpad * A_ROW; }
 __host__ __device__ constexpr int ring_slots(int rpad)
 {
     return (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad) > MAX_SLOTS
@@ -115,7 +122,7 @@ __host__ __device__ constexpr int ring_slots(int rpad)
 }
 // pair reduction area: per wave, for each 32-row block, two u4 per lane
 constexpr int RED_WAVE = (RMAX / 32) * 2 * 64 * 16;
-static_assert(ring_slots(RMAX) >= 2, "the tallest tile needs at least 2 ring slots");
+static_assert(ring_slots(RMAX) >= 3, "the tallest tile needs at least 3 ring slots");
 static_assert(8 * RED_WAVE <= LDS_BYTES, "pair-reduction area must fit in LDS");
 }  // namespace pk
 
@@ -185,35 +192,45 @@ __device__ __forceinline__ void barrier_lds()
 // A operand: raw bytes -> fp16 LDS buffer
 // ---------------------------------------------------------------------------------------
 
-// Dequantise the A bytes of the superstep held at `slot_base` into the fp16 buffer (natural
-// K order, A_ROW-byte rows), all 8 waves together.  Piece id = tid + 512 i covers row
-// id / 16, K values 16 (id % 16) .. +16 (8 code bytes, one scale byte).  Rows in
-// [rows, rpad) get scale 0, so they dequantise to zeros.
+// Dequantisation of half HALF of the superstep held in a ring slot into one fp16 buffer
+// (natural K order, A_ROW-byte rows), all 8 waves together, split into a read (issued
+// early) and the conversion and store (whose VALU work then overlaps MFMAs).  Every
+// thread takes NRB pieces: piece id = tid + 512 i covers row id / 16, K values 8 (id % 16)
+// .. +8 of the half (4 code bytes; one scale byte).  Rows in [rows, rpad) get scale 0,
+// so they dequantise to zeros.
 template <int NRB>
-__device__ __forceinline__ void pk_dequant_a(const uint8_t* slot_base, uint8_t* a16, int rows, int tid)
+struct ARaw {
+    uint32_t q[NRB];
+    uint32_t sc[NRB];
+};
+
+template <int NRB, int HALF>
+__device__ __forceinline__ void pk_read_a(ARaw<NRB>& a, const uint8_t* slot_base, int rows, int tid)
 {
     using namespace pk;
     constexpr int rpad = 32 * NRB;
     const uint8_t* codes = slot_base + A_CODES_AT;
     const uint8_t* scales = codes + rpad * ROWB;
-    u2_t q[NRB];
-    uint32_t sc[NRB];
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
         const int id = tid + THREADS * i;
-        const int r = id >> 4, p = id & 15;
-        q[i] = *reinterpret_cast<const u2_t*>(codes + r * ROWB + 16 * ((p >> 1) ^ (r & 7)) + 8 * (p & 1));
-        const uint32_t s8 = scales[r * SCB + p];
-        sc[i] = r < rows ? s8 : 0u;
+        const int r = id >> 4, hp = id & 15;
+        const int chunk = 4 * HALF + (hp >> 2);
+        a.q[i] = *reinterpret_cast<const uint32_t*>(codes + r * ROWB + 16 * (chunk ^ swz(r)) + 4 * (hp & 3));
+        const uint32_t s8 = scales[r * SCB + 8 * HALF + (hp >> 1)];
+        a.sc[i] = r < rows ? s8 : 0u;
     }
+}
+
+template <int NRB>
+__device__ __forceinline__ void pk_write_a(const ARaw<NRB>& a, uint8_t* dst, int tid)
+{
+    using namespace pk;
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
         const int id = tid + THREADS * i;
-        const int r = id >> 4, p = id & 15;
-        u4_t* d = reinterpret_cast<u4_t*>(a16 + r * A_ROW + 32 * p);
-        const h2_t s2 = scale_pair(sc[i]);
-        d[0] = dequant8(q[i].x, s2);
-        d[1] = dequant8(q[i].y, s2);
+        const int r = id >> 4, hp = id & 15;
+        *reinterpret_cast<u4_t*>(dst + r * A_ROW + 16 * hp) = dequant8(a.q[i], scale_pair(a.sc[i]));
     }
 }
 
@@ -229,14 +246,23 @@ struct BRaw {
     uint32_t w;
 };
 
+// Code bytes of compute step U: the whole 16-byte chunk 2U + h of the row is read (that
+// is conflict-free across 16 rows, half of it would not be) and the wave's half kept.
 template <int U>
-__device__ __forceinline__ void pk_read_b(BRaw& r, const uint8_t* slot_base, int cb, int lane, int x)
+__device__ __forceinline__ u2_t pk_read_b(const uint8_t* slot_base, int cb, int lane, int x)
 {
     using namespace pk;
     const int j = lane & 31, h = lane >> 5;
     const int row = 32 * cb + j;
-    r.q = *reinterpret_cast<const u2_t*>(slot_base + row * ROWB + 16 * ((2 * U + h) ^ (row & 7)) + 8 * x);
-    r.w = *reinterpret_cast<const uint32_t*>(slot_base + B_SCALES_AT + row * SCB + 4 * U);
+    const u4_t c = *reinterpret_cast<const u4_t*>(slot_base + row * ROWB + 16 * ((2 * U + h) ^ swz(row)));
+    return x ? u2_t{c.z, c.w} : u2_t{c.x, c.y};
+}
+
+// The row's 16 scale bytes of a superstep (word U belongs to compute step U).
+__device__ __forceinline__ u4_t pk_read_bs(const uint8_t* slot_base, int cb, int lane)
+{
+    using namespace pk;
+    return *reinterpret_cast<const u4_t*>(slot_base + B_SCALES_AT + (32 * cb + (lane & 31)) * SCB);
 }
 
 // Dequantise both sub-steps of the raw B operand.  `bsel` is a byte selector that copies
@@ -253,30 +279,80 @@ __device__ __forceinline__ void pk_dequant_b(h8_t (&bf)[2], const BRaw& r, uint3
 // Compute steps
 // ---------------------------------------------------------------------------------------
 
-// Compute step U of the superstep held at `cur` (A in the fp16 buffer).  On entry `b`
-// holds the raw B operand of step U; for U < 3 it holds that of step U + 1 on exit (read
-// here, ahead of its use, so that the read overlaps this step's work).
-template <int NRB, int U>
-__device__ __forceinline__ void pk_step(f16v_t (&acc)[NRB], BRaw& b, const uint8_t* cur, const uint8_t* arow,
-                                        uint32_t bsel, int cb, int lane, int x)
+// MFMAs of one compute step: B fragments bf (sub-steps 0, 1), A fragments af.
+template <int NRB>
+__device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[NRB], const h8_t (&bf)[2], const h8_t (&af)[2][NRB])
 {
-    using namespace pk;
-    h8_t af[2][NRB];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            af[i][rb] = *reinterpret_cast<const h8_t*>(arow + rb * 32 * A_ROW + 2 * BK * U + 16 * i);
-    BRaw bn;
-    if constexpr (U + 1 < SUB) pk_read_b<U + 1>(bn, cur, cb, lane, x);
-    h8_t bf[2];
-    pk_dequant_b(bf, b, bsel);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb)
             acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[i], af[i][rb], acc[rb], 0, 0, 0);
-    if constexpr (U + 1 < SUB) b = bn;
+}
+
+// Ask the scheduler to interleave the MFMAs of a step with the VALU work issued beside
+// them (one MFMA, then V VALU instructions, repeated), so that the dequantisation of the
+// next operands runs while the matrix core works.
+template <int NMFMA, int V>
+__device__ __forceinline__ void pk_interleave()
+{
+#pragma unroll
+    for (int m = 0; m < NMFMA; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
+    }
+}
+
+// One half superstep (compute steps U0 = 2 HALF and U0 + 1 of the superstep in `cur`, A
+// in fp16 buffer `ahalf`).  On entry `bf` holds the dequantised B operand of step U0 and
+// `bnext` the raw B operand of step U0 + 1; on exit they hold those of the first two steps
+// of the next half (from `cur` for HALF = 0, from the next superstep `nxt` for HALF = 1).
+// `sw` holds the B scale words of the current superstep (HALF = 0) and is replaced by
+// those of the next one during HALF = 1.
+// Meanwhile half `next half` of A is dequantised into `anext` (all threads share it).
+// The reads for the next half come first, then the MFMAs of each step interleaved with
+// the dequantisation of the operand that follows.
+template <int NRB, int HALF>
+__device__ __forceinline__ void pk_half(f16v_t (&acc)[NRB], h8_t (&bf)[2], BRaw& bnext, u4_t& sw, const uint8_t* cur,
+                                        const uint8_t* nxt, const uint8_t* ahalf, uint8_t* anext, int rows,
+                                        uint32_t bsel, int cb, int lane, int x, int tid)
+{
+    using namespace pk;
+    h8_t af0[2][NRB], af1[2][NRB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            af0[i][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW + 16 * i);
+            af1[i][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW + 2 * BK + 16 * i);
+        }
+    BRaw b2, b3;   // raw B of the next half's two steps
+    ARaw<NRB> an;  // raw A of the next half
+    if constexpr (HALF == 0) {
+        b2.q = pk_read_b<2>(cur, cb, lane, x);
+        b3.q = pk_read_b<3>(cur, cb, lane, x);
+        b2.w = sw[2];
+        b3.w = sw[3];
+        pk_read_a<NRB, 1>(an, cur, rows, tid);
+    } else {
+        sw = pk_read_bs(nxt, cb, lane);
+        b2.q = pk_read_b<0>(nxt, cb, lane, x);
+        b3.q = pk_read_b<1>(nxt, cb, lane, x);
+        b2.w = sw[0];
+        b3.w = sw[1];
+        pk_read_a<NRB, 0>(an, nxt, rows, tid);
+    }
+    // step U0: MFMAs beside the dequantisation of step U0 + 1
+    h8_t bf1[2];
+    pk_mfmas<NRB>(acc, bf, af0);
+    pk_dequant_b(bf1, bnext, bsel);
+    pk_interleave<2 * NRB, 18 / (2 * NRB)>();
+    // step U0 + 1: MFMAs beside the dequantisation of the next half's first step and of A
+    pk_mfmas<NRB>(acc, bf1, af1);
+    pk_dequant_b(bf, b2, bsel);
+    pk_write_a<NRB>(an, anext, tid);
+    pk_interleave<2 * NRB, (18 + 10 * NRB) / (2 * NRB)>();
+    bnext = b3;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -343,7 +419,7 @@ __device__ __forceinline__ void pk_reduce_store(f16v_t (&acc)[NRB], uint8_t* sme
 // 8 waves execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs
 // per B fragment.
 template <int NRB>
-__device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_, uint8_t* smem)
+__device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_, uint8_t* smem)
 {
     using namespace pk;
     // workgroup-uniform scalars (the call passes them in vector registers)
@@ -364,7 +440,7 @@ __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row
 
     // this wave's loads (see SuperLoads); lane l of a code instruction covers row
     // (first row + l / 8) and stores LDS chunk l % 8, which holds global chunk
-    // (l % 8) ^ (row & 7)
+    // (l % 8) ^ swz(row)
     SuperLoads L;
     {
         const int rl = lane >> 3, pos = lane & 7;
@@ -372,7 +448,7 @@ __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row
         for (int q = 0; q < 2; ++q) {
             const int i = wave + 8 * q;   // B code instruction
             const int r = 8 * i + rl;
-            L.b[q] = G.b + (long)min(col0 + r, n - 1) * qs + 16 * (pos ^ (r & 7));
+            L.b[q] = G.b + (long)min(col0 + r, n - 1) * qs + 16 * (pos ^ swz(r));
             L.b_dst[q] = 8 * i * ROWB;
         }
         L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
@@ -384,7 +460,7 @@ __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row
         for (int q = 0; q < 2; ++q) {
             const int a = ((wave + 4) & 7) + 8 * q;   // A code instruction
             const int r = 8 * a + rl;
-            L.a[q] = G.a + (long)(row0 + min(r, rows - 1)) * qs + 16 * (pos ^ (r & 7));
+            L.a[q] = G.a + (long)(row0 + min(r, rows - 1)) * qs + 16 * (pos ^ swz(r));
             L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
             if (a < na_total) L.na = q + 1;
         }
@@ -399,42 +475,58 @@ __device__ __noinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) acc[rb] = f16v_t{};
 
-    // prologue: supersteps 0 .. nslots-1 in flight; wait for superstep 0; dequantise its A
-    // and read the raw B operand of its first step
+    // prologue: superstep 0 first, on its own, so that it does not queue behind the others
+    // in a memory system that every CU floods at the same moment; then supersteps
+    // 1 .. nslots-1; dequantise the A of superstep 0's first half and read the raw B
+    // operand of its first step
     const int first = min(nslots, supers);
-    for (int t = 0; t < first; ++t) pk_issue(ring + t * sbytes, t, L, lane);
-    pk_wait_loads((first - 1) * L.ops);
+    pk_issue(ring, 0, L, lane);
+    pk_wait_loads(0);
+    for (int t = 1; t < first; ++t) pk_issue(ring + t * sbytes, t, L, lane);
     barrier_lds();
-    BRaw b;
-    pk_read_b<0>(b, ring, cb, lane, x);
-    pk_dequant_a<NRB>(ring, a16, rows, tid);
+    uint8_t* a16h[2] = {a16, a16 + rpad * A_ROW};
+    const int aoff = j * A_ROW + 64 * h + 32 * x;   // this lane's A fragment row
+    const uint32_t bsel = 0x0c0c0000u | ((uint32_t)(2 * h + x) << 8) | (uint32_t)(2 * h + x);
+    h8_t bf[2];
+    BRaw bnext;
+    u4_t sw = pk_read_bs(ring, cb, lane);
+    {
+        BRaw b0;
+        b0.q = pk_read_b<0>(ring, cb, lane, x);
+        b0.w = sw[0];
+        bnext.q = pk_read_b<1>(ring, cb, lane, x);
+        bnext.w = sw[1];
+        ARaw<NRB> a0;
+        pk_read_a<NRB, 0>(a0, ring, rows, tid);
+        pk_dequant_b(bf, b0, bsel);
+        pk_write_a<NRB>(a0, a16h[0], tid);
+    }
     barrier_lds();
 
-    const uint8_t* arow = a16 + j * A_ROW + 64 * h + 32 * x;   // this lane's A fragment row
-    const uint32_t bsel = 0x0c0c0000u | ((uint32_t)(2 * h + x) << 8) | (uint32_t)(2 * h + x);
     int cs = 0;   // slot of superstep t
     for (int t = 0; t < supers; ++t) {
+        // the slot of superstep t - 1 is free since the last barrier: refill it with
+        // superstep t - 1 + nslots
+        if (t > 0 && t - 1 + nslots < supers) {
+            const int fs = (cs == 0) ? nslots - 1 : cs - 1;
+            pk_issue(ring + fs * sbytes, t - 1 + nslots, L, lane);
+        }
+        const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
         const uint8_t* cur = ring + cs * sbytes;
-        pk_step<NRB, 0>(acc, b, cur, arow, bsel, cb, lane, x);
-        pk_step<NRB, 1>(acc, b, cur, arow, bsel, cb, lane, x);
-        pk_step<NRB, 2>(acc, b, cur, arow, bsel, cb, lane, x);
-        pk_step<NRB, 3>(acc, b, cur, arow, bsel, cb, lane, x);
+        // after the last superstep the "next" reads land on a slot that holds no data any
+        // more: harmless, and their results are unused
+        const uint8_t* nxt = ring + ns * sbytes;
+        pk_half<NRB, 0>(acc, bf, bnext, sw, cur, nxt, a16h[0] + aoff, a16h[1], rows, bsel, cb, lane, x, tid);
+        // superstep t + 1 must have landed before half 1 reads its bytes
         if (t + 1 < supers) {
-            // superstep t + 1 must have landed; after the barrier nobody reads superstep
-            // t's slot or the fp16 A buffer any more
             const int last = min(supers - 1, t - 1 + nslots);   // last superstep issued
             pk_wait_loads((last - (t + 1)) * L.ops);
-            barrier_lds();
-            if (t + nslots < supers) pk_issue(ring + cs * sbytes, t + nslots, L, lane);
-            cs = (cs + 1 == nslots) ? 0 : cs + 1;
-            const uint8_t* nxt = ring + cs * sbytes;
-            pk_read_b<0>(b, nxt, cb, lane, x);
-            pk_dequant_a<NRB>(nxt, a16, rows, tid);
-            barrier_lds();
         }
+        barrier_lds();
+        pk_half<NRB, 1>(acc, bf, bnext, sw, cur, nxt, a16h[1] + aoff, a16h[0], rows, bsel, cb, lane, x, tid);
+        barrier_lds();
+        cs = ns;
     }
-    // every wave is past its last LDS read of the loop
-    barrier_lds();
 
     // all loads have landed (the last superstep was waited for) and no wave reads the ring
     // any more: the reduction area may overwrite it
@@ -454,7 +546,9 @@ __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args
     (void)args_byval;
     const KernArgs& args = *(const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     const int b = blockIdx.x;
-    for (int i = args.wg_begin[b]; i < args.wg_begin[b + 1]; ++i) {
+    // (read once: the C stores of a tile could alias these as far as the compiler knows)
+    const int i_begin = args.wg_begin[b], i_end = args.wg_begin[b + 1];
+    for (int i = i_begin; i < i_end; ++i) {
         // the tile is workgroup-uniform: keep it in scalar registers so that the group
         // table is read from the kernel arguments with scalar loads
         const TileDesc tv = args.tiles[i];
@@ -466,7 +560,6 @@ __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args
         case 1: pk_tile<1>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         case 2: pk_tile<2>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         case 3: pk_tile<3>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 4: pk_tile<4>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         default: break;
         }
     }
