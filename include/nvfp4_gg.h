@@ -23,7 +23,9 @@
  *   C_i   [m_i][n] fp16 (IEEE binary16).
  * n and k are the same for every group; m_i varies (m_i = 0 is allowed and writes nothing).
  *
- * Ownership: the caller owns every device buffer.  A plan owns host memory only.
+ * Ownership: the caller owns every device buffer it passes.  A plan owns host memory and
+ * one small device buffer on its device (its tile schedule: 16 bytes per tile and 4 bytes
+ * per workgroup), allocated by nvfp4_gg_plan and freed by nvfp4_gg_destroy.
  * Asynchrony: nvfp4_gg_run only enqueues work on the given stream; it never synchronises,
  * allocates device memory, prints or throws.
  * Threading: a plan is immutable after nvfp4_gg_plan returns; several threads may call
@@ -66,7 +68,7 @@ typedef struct {
     int g, n, k;
     int device;            /* HIP device ordinal, or NVFP4_GG_DEVICE_NONE */
     int num_cus;           /* compute units the schedule was sized for */
-    int tile_m, tile_n;    /* output tile of one workgroup */
+    int tile_m, tile_n;    /* largest output tile of one workgroup (rows, columns) */
     int total_tiles;       /* tiles over all groups */
     int grid;              /* workgroups launched per call */
     int block;             /* threads per workgroup */
@@ -78,11 +80,14 @@ typedef struct {
 
 /*
  * Build a plan for g groups with row counts m[0..g-1] (host array, copied), and shared
- * n and k.  Host-only work: validation, per-group tile counts, the largest-work-first
- * group order and its tile prefix sum (the host planning of custom_kernel on the page
- * "kernelindex submission 503584": groups sorted by tile work, prefix of per-group tile
- * counts), and the launch shape.
- *   device: HIP device ordinal, -1 for the current device, or NVFP4_GG_DEVICE_NONE.
+ * n and k: validation, the largest-work-first group order and its tile prefix sum (the
+ * host planning of custom_kernel on the page "kernelindex submission 503584": groups
+ * sorted by tile work, prefix of per-group tile counts), the tile height, and a balanced
+ * schedule of the tiles over the device's workgroups, which is uploaded once to device
+ * memory owned by the plan (synchronous hipMalloc + hipMemcpy; allocation failure:
+ * NVFP4_GG_ENOMEM).  Plans are meant to be built once per shape and reused.
+ *   device: HIP device ordinal, -1 for the current device, or NVFP4_GG_DEVICE_NONE (host
+ *   only: nothing is allocated on a device).
  * Requirements: 1 <= g <= NVFP4_GG_MAX_GROUPS, n >= 1, k >= 256 and k % 256 == 0 (the
  * K granularity the group_gemm host function of "kernelindex submission 498317"
  * requires), 0 <= m_i <= 2^20; else NVFP4_GG_EINVAL (g above the maximum:
@@ -110,7 +115,9 @@ nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan,
 /* Copy the plan's decisions into *info.  NVFP4_GG_EINVAL on a null argument. */
 nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_plan_info_t* info);
 
-/* Release a plan (NULL is ignored).  Work already enqueued by nvfp4_gg_run is unaffected. */
+/* Release a plan (NULL is ignored).  Waits until the plan's device has finished its
+ * outstanding work (an enqueued call may still read the plan's schedule), then frees the
+ * plan's device and host memory. */
 void nvfp4_gg_destroy(nvfp4_gg_plan_t plan);
 
 /* Static English text for a status code; never NULL. */

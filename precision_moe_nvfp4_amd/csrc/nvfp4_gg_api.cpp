@@ -160,10 +160,18 @@ extern "C" const char* nvfp4_gg_status_string(nvfp4_gg_status_t s)
     return "unknown status";
 }
 
+// Free the plan's device schedule on its device, after that device has finished the work
+// already enqueued (a launch may still be reading the schedule).
 static void free_device(nvfp4_gg_plan_s* p)
 {
+    if (p->d_tiles == nullptr && p->d_wg_begin == nullptr) return;
+    int prev = -1;
+    const bool switch_dev = hipGetDevice(&prev) == hipSuccess && prev != p->device;
+    if (switch_dev) (void)hipSetDevice(p->device);
+    (void)hipDeviceSynchronize();
     if (p->d_tiles) (void)hipFree(p->d_tiles);
     if (p->d_wg_begin) (void)hipFree(p->d_wg_begin);
+    if (switch_dev) (void)hipSetDevice(prev);
     p->d_tiles = nullptr;
     p->d_wg_begin = nullptr;
 }
