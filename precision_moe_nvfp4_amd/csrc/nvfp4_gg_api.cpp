@@ -228,17 +228,25 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const in
         p->chunk_rows = best.chunk_rows;
         p->est_cycles = best.makespan;
 
-        // flatten: workgroup b's tiles, largest first; grid ends at the last busy workgroup
+        // flatten: tiles[b] is the first tile of workgroup b (rows = 0 if it has none), so
+        // that a workgroup can fetch it without first reading its range; the further tiles
+        // of workgroup b follow at tiles[wg_begin[b] .. wg_begin[b+1]).  The grid ends at the
+        // last busy workgroup.
         int last = -1;
         for (int b = 0; b < num_cus; ++b)
             if (!best.per_wg[b].empty()) last = b;
         p->grid = last + 1;
-        p->wg_begin.assign(p->grid + 1, 0);
+        p->tiles.assign(p->grid, TileDesc{0, 0, 0, 0});
+        p->wg_begin.assign(p->grid + 1, p->grid);
         for (int b = 0; b < p->grid; ++b) {
-            for (const auto& t : best.per_wg[b]) p->tiles.push_back(t);
-            p->wg_begin[b + 1] = (int)p->tiles.size();
+            const auto& v = best.per_wg[b];
+            if (!v.empty()) p->tiles[b] = v[0];
+            p->wg_begin[b] = (int)p->tiles.size();
+            for (size_t i = 1; i < v.size(); ++i) p->tiles.push_back(v[i]);
         }
-        p->total_tiles = (int)p->tiles.size();
+        p->wg_begin[p->grid] = (int)p->tiles.size();
+        p->total_tiles = 0;
+        for (const auto& t : p->tiles) p->total_tiles += t.rows > 0 ? 1 : 0;
 
         // informational per-group tile prefix (schedule order)
         p->tile_begin.assign(g + 1, 0);

@@ -21,7 +21,7 @@ struct GroupArgs {
 };
 
 // One output tile: rows [row0, row0 + rows) of group `group` (schedule index), columns
-// [col0, col0 + 256).
+// [col0, col0 + 128).
 struct TileDesc {
     int group;
     int row0;
@@ -36,8 +36,8 @@ struct KernArgs {
     int n;
     int k;
     int ntiles;
-    const TileDesc* tiles;  // tiles in processing order, grouped by workgroup
-    const int* wg_begin;    // workgroup b processes tiles[wg_begin[b] .. wg_begin[b+1])
+    const TileDesc* tiles;  // tiles[b]: first tile of workgroup b (rows = 0: none)
+    const int* wg_begin;    // workgroup b then processes tiles[wg_begin[b] .. wg_begin[b+1])
     GroupArgs grp[NVFP4_GG_MAX_GROUPS];
 };
 static_assert(sizeof(KernArgs) <= 4096, "kernel arguments must fit the 4 KiB kernarg segment");

@@ -13,9 +13,10 @@
 //
 // Structure: a persistent grid (one workgroup of 8 waves, 2 per SIMD, per CU) walks a tile
 // list built by the host planner.  A tile is up to 96 rows of one group x 128 columns.
-// Wave w owns the 32 columns 32 (w & 3) .. +32 and all tile rows; the waves w and w + 4
-// split every K step between them.  So each dequantised B fragment feeds one MFMA per 32
-// tile rows, and each A fragment read from LDS feeds one MFMA:
+// Wave w owns the 64 columns 64 (w & 1) .. +64 and all tile rows, and one quarter of every
+// K step (w >> 1); the four partial sums of a column half are added through LDS at the
+// end.  So each dequantised B fragment feeds one MFMA per 32 tile rows, and each A
+// fragment read from LDS feeds two MFMAs:
 //   * An LDS ring receives, per superstep of K = 256, the raw bytes of the superstep (B
 //     rows, A rows and their scales) straight from HBM through direct-to-LDS loads (no
 //     VGPR staging), one whole 128-byte line per row and load instruction; 3 or 4
@@ -24,13 +25,14 @@
 //   * A (shared by the waves) is dequantised once per workgroup, by all 8 waves, into a
 //     double-buffered fp16 LDS buffer holding half a superstep (K = 128), one half ahead of
 //     its use, and read back as MFMA fragments.
-//   * The 2 compute steps (K = 64) of a half run without barriers; the dequantisation of
-//     the next half overlaps their MFMAs.
+//   * The 2 compute steps (K = 64) of a half run without barriers, from B fragments
+//     dequantised during the previous half; the MFMAs are interleaved with the
+//     dequantisation of the next half's operands.
 //   * v_mfma_f32_32x32x16_f16 takes the B fragment as its M-side operand, so each lane
 //     ends up holding runs of 4 consecutive C columns (8-byte fp16 stores).
-// K is permuted inside each compute step, identically for A and B (the dot product is
-// unchanged): lane half h, wave pair x and sub-step i take the 8 K values starting at
-// 32h + 16x + 8i.
+// K is permuted inside each half superstep, identically for A and B (the dot product is
+// unchanged): lane half h, K quarter t and step u take the 8 K values starting at
+// 64h + 16t + 8u, so that a lane's B bytes of a whole half are 8 contiguous bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,9 +84,9 @@ __device__ __forceinline__ u4_t dequant8(uint32_t x, h2_t s)
 // ---------------------------------------------------------------------------------------
 namespace pk {
 constexpr int THREADS = 512;         // 8 waves, 2 per SIMD
-constexpr int BN = 128;              // tile columns: wave w owns columns 32 (w & 3) .. +32
+constexpr int BN = 128;              // tile columns: wave w owns columns 64 (w & 1) .. +64
 constexpr int RMAX = 96;             // tile rows (multiple of 32)
-constexpr int BK = 64;               // K per compute step (4 MFMA sub-steps of 16)
+
 constexpr int SK = 256;              // K per load superstep
 constexpr int HK = SK / 2;           // K per half superstep (one fp16 A buffer)
 constexpr int ROWB = SK / 2;         // code bytes per row and superstep: one 128-byte line
@@ -120,10 +122,11 @@ __host__ __device__ constexpr int ring_slots(int rpad)
                ? MAX_SLOTS
                : (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad);
 }
-// pair reduction area: per wave, for each 32-row block, two u4 per lane
-constexpr int RED_WAVE = (RMAX / 32) * 2 * 64 * 16;
+// reduction area: per wave, for each column block and 32-row block, the three element
+// groups handed to the other K quarters (one u4 per lane each)
+constexpr int RED_WAVE = 2 * (RMAX / 32) * 3 * 64 * 16;
 static_assert(ring_slots(RMAX) >= 3, "the tallest tile needs at least 3 ring slots");
-static_assert(8 * RED_WAVE <= LDS_BYTES, "pair-reduction area must fit in LDS");
+static_assert(8 * RED_WAVE <= LDS_BYTES, "reduction area must fit in LDS");
 }  // namespace pk
 
 // ---------------------------------------------------------------------------------------
@@ -196,8 +199,8 @@ __device__ __forceinline__ void barrier_lds()
 // (natural K order, A_ROW-byte rows), all 8 waves together, split into a read (issued
 // early) and the conversion and store (whose VALU work then overlaps MFMAs).  Every
 // thread takes NRB pieces: piece id = tid + 512 i covers row id / 16, K values 8 (id % 16)
-// .. +8 of the half (4 code bytes; one scale byte).  Rows in [rows, rpad) get scale 0,
-// so they dequantise to zeros.
+// .. +8 of the half (4 code bytes; one scale byte).  Rows in [rows, rpad) repeat the last
+// row (the loads clamp to it); their results land in tile rows that are never stored.
 template <int NRB>
 struct ARaw {
     uint32_t q[NRB];
@@ -217,8 +220,8 @@ __device__ __forceinline__ void pk_read_a(ARaw<NRB>& a, const uint8_t* slot_base
         const int r = id >> 4, hp = id & 15;
         const int chunk = 4 * HALF + (hp >> 2);
         a.q[i] = *reinterpret_cast<const uint32_t*>(codes + r * ROWB + 16 * (chunk ^ swz(r)) + 4 * (hp & 3));
-        const uint32_t s8 = scales[r * SCB + 8 * HALF + (hp >> 1)];
-        a.sc[i] = r < rows ? s8 : 0u;
+        a.sc[i] = scales[r * SCB + 8 * HALF + (hp >> 1)];
+        (void)rows;
     }
 }
 
@@ -238,177 +241,169 @@ __device__ __forceinline__ void pk_write_a(const ARaw<NRB>& a, uint8_t* dst, int
 // B operand: raw bytes -> registers
 // ---------------------------------------------------------------------------------------
 
-// One wave's raw B operand of a compute step: the lane's 8 code bytes of row 32 cb + j for
-// its two sub-steps (K values 32h + 16x .. +16 of the step, one 16-value scale block) and
-// the row's scale word of the step (4 bytes, one per 16 K values).
-struct BRaw {
-    u2_t q;
-    uint32_t w;
-};
-
-// Code bytes of compute step U: the whole 16-byte chunk 2U + h of the row is read (that
-// is conflict-free across 16 rows, half of it would not be) and the wave's half kept.
-template <int U>
-__device__ __forceinline__ u2_t pk_read_b(const uint8_t* slot_base, int cb, int lane, int x)
+// The lane's 8 B code bytes of half HALF of the superstep in `slot_base`, for the tile's
+// column block c (row 32 c + j): K values 64h + 16t + 8u .. +8 for steps u = 0, 1 (dword u).
+template <int HALF>
+__device__ __forceinline__ u2_t pk_read_b(const uint8_t* slot_base, int c, int lane, int t)
 {
     using namespace pk;
     const int j = lane & 31, h = lane >> 5;
-    const int row = 32 * cb + j;
-    const u4_t c = *reinterpret_cast<const u4_t*>(slot_base + row * ROWB + 16 * ((2 * U + h) ^ swz(row)));
-    return x ? u2_t{c.z, c.w} : u2_t{c.x, c.y};
+    const int row = 32 * c + j;
+    const int chunk = 4 * HALF + 2 * h + (t >> 1);
+    return *reinterpret_cast<const u2_t*>(slot_base + row * ROWB + 16 * (chunk ^ swz(row)) + 8 * (t & 1));
 }
 
-// The row's 16 scale bytes of a superstep (word U belongs to compute step U).
-__device__ __forceinline__ u4_t pk_read_bs(const uint8_t* slot_base, int cb, int lane)
+// The two scale words of row 32 c + j that this lane needs in a superstep: words h and
+// 2 + h of the row's 16 scale bytes (half 0 and half 1).
+__device__ __forceinline__ u2_t pk_read_bs(const uint8_t* slot_base, int c, int lane)
 {
     using namespace pk;
-    return *reinterpret_cast<const u4_t*>(slot_base + B_SCALES_AT + (32 * cb + (lane & 31)) * SCB);
+    const uint32_t* w =
+        reinterpret_cast<const uint32_t*>(slot_base + B_SCALES_AT + (32 * c + (lane & 31)) * SCB) + (lane >> 5);
+    return u2_t{w[0], w[2]};
 }
 
-// Dequantise both sub-steps of the raw B operand.  `bsel` is a byte selector that copies
-// this lane's scale byte (byte 2h + x of the word) into bytes 0 and 1.
-__device__ __forceinline__ void pk_dequant_b(h8_t (&bf)[2], const BRaw& r, uint32_t bsel)
+// fp16 scale pair (column block 0, column block 1) of half HALF: byte 8 HALF + 4h + t of
+// each row's scale bytes, i.e. byte t of the lane's word for that half.
+template <int HALF>
+__device__ __forceinline__ h2_t pk_scales(const u2_t (&srow)[2], uint32_t tsel)
 {
-    const uint32_t pair = __builtin_amdgcn_perm(0u, r.w, bsel);
-    const h2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false);
-    bf[0] = __builtin_bit_cast(h8_t, dequant8(r.q.x, sc));
-    bf[1] = __builtin_bit_cast(h8_t, dequant8(r.q.y, sc));
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(srow[1][HALF], srow[0][HALF], tsel), 1.0f,
+                                                    false);
 }
 
 // ---------------------------------------------------------------------------------------
-// Compute steps
+// Compute
 // ---------------------------------------------------------------------------------------
 
-// MFMAs of one compute step: B fragments bf (sub-steps 0, 1), A fragments af.
+// MFMAs of one step: B fragments of the two column blocks, A fragments of the row blocks.
 template <int NRB>
-__device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[NRB], const h8_t (&bf)[2], const h8_t (&af)[2][NRB])
+__device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[2][NRB], const h8_t (&bf)[2], const h8_t (&af)[NRB])
 {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[i], af[i][rb], acc[rb], 0, 0, 0);
+        for (int c = 0; c < 2; ++c)
+            acc[c][rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c], af[rb], acc[c][rb], 0, 0, 0);
 }
 
-// Ask the scheduler to interleave the MFMAs of a step with the VALU work issued beside
-// them (one MFMA, then V VALU instructions, repeated), so that the dequantisation of the
-// next operands runs while the matrix core works.
-template <int NMFMA, int V>
-__device__ __forceinline__ void pk_interleave()
-{
-#pragma unroll
-    for (int m = 0; m < NMFMA; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
-    }
-}
-
-// One half superstep (compute steps U0 = 2 HALF and U0 + 1 of the superstep in `cur`, A
-// in fp16 buffer `ahalf`).  On entry `bf` holds the dequantised B operand of step U0 and
-// `bnext` the raw B operand of step U0 + 1; on exit they hold those of the first two steps
-// of the next half (from `cur` for HALF = 0, from the next superstep `nxt` for HALF = 1).
-// `sw` holds the B scale words of the current superstep (HALF = 0) and is replaced by
-// those of the next one during HALF = 1.
-// Meanwhile half `next half` of A is dequantised into `anext` (all threads share it).
-// The reads for the next half come first, then the MFMAs of each step interleaved with
-// the dequantisation of the operand that follows.
+// One half superstep (steps u = 0, 1 of half HALF of the superstep in `cur`, A in the fp16
+// buffer at `ahalf`, B fragments bf[u][c] dequantised during the previous half).  While its
+// MFMAs run, the next half's B fragments are dequantised into bf (from half 1 of `cur`, or
+// half 0 of the next superstep `nxt`, whose scale rows replace `srow` when HALF = 1) and
+// the next half of A into `anext` (all threads share that work), so that no MFMA waits
+// for VALU work of its own half.  The LDS reads come first.  The compiler's own schedule
+// of the independent MFMA and VALU streams is kept: forcing a strict MFMA/VALU
+// alternation with scheduling-group barriers measured 6-10% slower.
 template <int NRB, int HALF>
-__device__ __forceinline__ void pk_half(f16v_t (&acc)[NRB], h8_t (&bf)[2], BRaw& bnext, u4_t& sw, const uint8_t* cur,
+__device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], u2_t (&srow)[2], const uint8_t* cur,
                                         const uint8_t* nxt, const uint8_t* ahalf, uint8_t* anext, int rows,
-                                        uint32_t bsel, int cb, int lane, int x, int tid)
+                                        uint32_t tsel, int cb0, int lane, int t, int tid)
 {
     using namespace pk;
-    h8_t af0[2][NRB], af1[2][NRB];
+    h8_t af[2][NRB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            af0[i][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW + 16 * i);
-            af1[i][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW + 2 * BK + 16 * i);
-        }
-    BRaw b2, b3;   // raw B of the next half's two steps
-    ARaw<NRB> an;  // raw A of the next half
+    for (int rb = 0; rb < NRB; ++rb) {
+        af[0][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW);
+        af[1][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW + 16);
+    }
+    u2_t qn[2];     // raw B codes of the next half
+    ARaw<NRB> an;   // raw A of the next half
     if constexpr (HALF == 0) {
-        b2.q = pk_read_b<2>(cur, cb, lane, x);
-        b3.q = pk_read_b<3>(cur, cb, lane, x);
-        b2.w = sw[2];
-        b3.w = sw[3];
+        qn[0] = pk_read_b<1>(cur, cb0, lane, t);
+        qn[1] = pk_read_b<1>(cur, cb0 + 1, lane, t);
         pk_read_a<NRB, 1>(an, cur, rows, tid);
     } else {
-        sw = pk_read_bs(nxt, cb, lane);
-        b2.q = pk_read_b<0>(nxt, cb, lane, x);
-        b3.q = pk_read_b<1>(nxt, cb, lane, x);
-        b2.w = sw[0];
-        b3.w = sw[1];
+        srow[0] = pk_read_bs(nxt, cb0, lane);
+        srow[1] = pk_read_bs(nxt, cb0 + 1, lane);
+        qn[0] = pk_read_b<0>(nxt, cb0, lane, t);
+        qn[1] = pk_read_b<0>(nxt, cb0 + 1, lane, t);
         pk_read_a<NRB, 0>(an, nxt, rows, tid);
     }
-    // step U0: MFMAs beside the dequantisation of step U0 + 1
-    h8_t bf1[2];
-    pk_mfmas<NRB>(acc, bf, af0);
-    pk_dequant_b(bf1, bnext, bsel);
-    pk_interleave<2 * NRB, 18 / (2 * NRB)>();
-    // step U0 + 1: MFMAs beside the dequantisation of the next half's first step and of A
-    pk_mfmas<NRB>(acc, bf1, af1);
-    pk_dequant_b(bf, b2, bsel);
+    pk_mfmas<NRB>(acc, bf[0], af[0]);
+    pk_mfmas<NRB>(acc, bf[1], af[1]);
+    const h2_t sc = pk_scales<1 - HALF>(srow, tsel);
+    const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
     pk_write_a<NRB>(an, anext, tid);
-    pk_interleave<2 * NRB, (18 + 10 * NRB) / (2 * NRB)>();
-    bnext = b3;
+    bf[0][0] = __builtin_bit_cast(h8_t, dequant8(qn[0].x, s0));
+    bf[0][1] = __builtin_bit_cast(h8_t, dequant8(qn[1].x, s1));
+    bf[1][0] = __builtin_bit_cast(h8_t, dequant8(qn[0].y, s0));
+    bf[1][1] = __builtin_bit_cast(h8_t, dequant8(qn[1].y, s1));
 }
 
 // ---------------------------------------------------------------------------------------
 // Epilogue
 // ---------------------------------------------------------------------------------------
 
-// Pair reduction and store.  Lane (j, h) holds, in acc[rb] element 4q + e, the partial sum
-// of C[32 rb + j][32 cb + 8 q + 4 h + e].  Wave pair x keeps the element groups q = 2x,
-// 2x + 1 and hands the other two to its partner (wave w ^ 4) through LDS.
-template <int NRB, int KEEP>
-__device__ __forceinline__ void pk_reduce_store(f16v_t (&acc)[NRB], uint8_t* smem, uint16_t* __restrict__ c, int n,
-                                                int rows, int col, int wave, int lane)
+// Reduction over the four K quarters and store.  Lane (j, h) holds, in acc[c][rb] element
+// 4q + e, the partial sum of C[32 rb + j][64 cw + 32 c + 8 q + 4 h + e].  The wave with K
+// quarter t keeps element group q = t and hands the other three to the waves that keep
+// them (same column half) through LDS.
+template <int NRB>
+__device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uint8_t* smem, uint16_t* __restrict__ c0,
+                                                int n, int rows, int col, int wave, int lane)
 {
     using namespace pk;
-    constexpr int GIVE = 1 - KEEP;
+    const int cw = wave & 1, t = wave >> 1;
     u4_t* mine = reinterpret_cast<u4_t*>(smem + wave * RED_WAVE);
-    const u4_t* theirs = reinterpret_cast<const u4_t*>(smem + (wave ^ 4) * RED_WAVE);
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int q = 2 * GIVE + e;
-            mine[(rb * 2 + e) * 64 + lane] =
-                u4_t{__float_as_uint(acc[rb][4 * q + 0]), __float_as_uint(acc[rb][4 * q + 1]),
-                     __float_as_uint(acc[rb][4 * q + 2]), __float_as_uint(acc[rb][4 * q + 3])};
-        }
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q == t) continue;
+                const int slot = q - (q > t ? 1 : 0);
+                mine[((c * NRB + rb) * 3 + slot) * 64 + lane] =
+                    u4_t{__float_as_uint(acc[c][rb][4 * q + 0]), __float_as_uint(acc[c][rb][4 * q + 1]),
+                         __float_as_uint(acc[c][rb][4 * q + 2]), __float_as_uint(acc[c][rb][4 * q + 3])};
+            }
     barrier_lds();
     const int j = lane & 31, h = lane >> 5;
     const bool vec_ok = (n & 3) == 0;
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        const int r = rb * 32 + j;
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int q = 2 * KEEP + e;
-            const u4_t o = theirs[(rb * 2 + e) * 64 + lane];
-            // (element-wise __uint_as_float: __builtin_bit_cast of an ext-vector element
-            // reads element 0 with this compiler)
-            const uint16_t v0 = f16_bits_rne(acc[rb][4 * q + 0] + __uint_as_float(o.x));
-            const uint16_t v1 = f16_bits_rne(acc[rb][4 * q + 1] + __uint_as_float(o.y));
-            const uint16_t v2 = f16_bits_rne(acc[rb][4 * q + 2] + __uint_as_float(o.z));
-            const uint16_t v3 = f16_bits_rne(acc[rb][4 * q + 3] + __uint_as_float(o.w));
+        for (int rb = 0; rb < NRB; ++rb) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // acc element 4t + e; t is this wave's quarter (runtime), so pick it out
+                float a = acc[c][rb][e];
+                a = t == 1 ? acc[c][rb][4 + e] : a;
+                a = t == 2 ? acc[c][rb][8 + e] : a;
+                a = t == 3 ? acc[c][rb][12 + e] : a;
+                v[e] = a;
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                if (p == t) continue;
+                const int pw = cw + 2 * p;                      // partner wave
+                const int slot = t - (t > p ? 1 : 0);           // where the partner put group t
+                const u4_t o = reinterpret_cast<const u4_t*>(smem + pw * RED_WAVE)[((c * NRB + rb) * 3 + slot) * 64 + lane];
+                // (element-wise __uint_as_float: __builtin_bit_cast of an ext-vector element
+                // reads element 0 with this compiler)
+                v[0] += __uint_as_float(o.x);
+                v[1] += __uint_as_float(o.y);
+                v[2] += __uint_as_float(o.z);
+                v[3] += __uint_as_float(o.w);
+            }
+            const int r = rb * 32 + j;
             if (r >= rows) continue;
-            uint16_t* crow = c + (long)r * n;
-            const int cc = col + 8 * q + 4 * h;
+            const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
+            const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
+            uint16_t* crow = c0 + (long)r * n;
+            const int cc = col + 64 * cw + 32 * c + 8 * t + 4 * h;
             if (vec_ok && cc + 4 <= n) {
                 *reinterpret_cast<u2_t*>(crow + cc) =
-                    u2_t{(uint32_t)v0 | ((uint32_t)v1 << 16), (uint32_t)v2 | ((uint32_t)v3 << 16)};
+                    u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
             } else {
-                if (cc + 0 < n) crow[cc + 0] = v0;
-                if (cc + 1 < n) crow[cc + 1] = v1;
-                if (cc + 2 < n) crow[cc + 2] = v2;
-                if (cc + 3 < n) crow[cc + 3] = v3;
+                if (cc + 0 < n) crow[cc + 0] = h0;
+                if (cc + 1 < n) crow[cc + 1] = h1;
+                if (cc + 2 < n) crow[cc + 2] = h2;
+                if (cc + 3 < n) crow[cc + 3] = h3;
             }
         }
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -428,7 +423,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     const int col0 = __builtin_amdgcn_readfirstlane(col0_);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cb = wave & 3, x = wave >> 2;
+    const int cw = wave & 1, tq = wave >> 1;   // column half, K quarter
     const int j = lane & 31, h = lane >> 5;
     const int rpad = 32 * NRB;
     const int supers = k / SK;
@@ -471,9 +466,11 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         L.ops = 2 + L.nsb + L.na + L.nsa;
     }
 
-    f16v_t acc[NRB];
+    f16v_t acc[2][NRB];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) acc[rb] = f16v_t{};
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) acc[c][rb] = f16v_t{};
 
     // prologue: superstep 0 first, on its own, so that it does not queue behind the others
     // in a memory system that every CU floods at the same moment; then supersteps
@@ -485,20 +482,21 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     for (int t = 1; t < first; ++t) pk_issue(ring + t * sbytes, t, L, lane);
     barrier_lds();
     uint8_t* a16h[2] = {a16, a16 + rpad * A_ROW};
-    const int aoff = j * A_ROW + 64 * h + 32 * x;   // this lane's A fragment row
-    const uint32_t bsel = 0x0c0c0000u | ((uint32_t)(2 * h + x) << 8) | (uint32_t)(2 * h + x);
-    h8_t bf[2];
-    BRaw bnext;
-    u4_t sw = pk_read_bs(ring, cb, lane);
+    const int aoff = j * A_ROW + 128 * h + 32 * tq;   // this lane's A fragment row
+    const uint32_t tsel = 0x0c0c0000u | ((uint32_t)(4 + tq) << 8) | (uint32_t)tq;
+    const int cb0 = 2 * cw;
+    u2_t srow[2] = {pk_read_bs(ring, cb0, lane), pk_read_bs(ring, cb0 + 1, lane)};
+    h8_t bf[2][2];
     {
-        BRaw b0;
-        b0.q = pk_read_b<0>(ring, cb, lane, x);
-        b0.w = sw[0];
-        bnext.q = pk_read_b<1>(ring, cb, lane, x);
-        bnext.w = sw[1];
+        const u2_t q0 = pk_read_b<0>(ring, cb0, lane, tq), q1 = pk_read_b<0>(ring, cb0 + 1, lane, tq);
         ARaw<NRB> a0;
         pk_read_a<NRB, 0>(a0, ring, rows, tid);
-        pk_dequant_b(bf, b0, bsel);
+        const h2_t sc = pk_scales<0>(srow, tsel);
+        const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+        bf[0][0] = __builtin_bit_cast(h8_t, dequant8(q0.x, s0));
+        bf[0][1] = __builtin_bit_cast(h8_t, dequant8(q1.x, s1));
+        bf[1][0] = __builtin_bit_cast(h8_t, dequant8(q0.y, s0));
+        bf[1][1] = __builtin_bit_cast(h8_t, dequant8(q1.y, s1));
         pk_write_a<NRB>(a0, a16h[0], tid);
     }
     barrier_lds();
@@ -516,23 +514,21 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // after the last superstep the "next" reads land on a slot that holds no data any
         // more: harmless, and their results are unused
         const uint8_t* nxt = ring + ns * sbytes;
-        pk_half<NRB, 0>(acc, bf, bnext, sw, cur, nxt, a16h[0] + aoff, a16h[1], rows, bsel, cb, lane, x, tid);
+        pk_half<NRB, 0>(acc, bf, srow, cur, nxt, a16h[0] + aoff, a16h[1], rows, tsel, cb0, lane, tq, tid);
         // superstep t + 1 must have landed before half 1 reads its bytes
         if (t + 1 < supers) {
             const int last = min(supers - 1, t - 1 + nslots);   // last superstep issued
             pk_wait_loads((last - (t + 1)) * L.ops);
         }
         barrier_lds();
-        pk_half<NRB, 1>(acc, bf, bnext, sw, cur, nxt, a16h[1] + aoff, a16h[0], rows, bsel, cb, lane, x, tid);
+        pk_half<NRB, 1>(acc, bf, srow, cur, nxt, a16h[1] + aoff, a16h[0], rows, tsel, cb0, lane, tq, tid);
         barrier_lds();
         cs = ns;
     }
 
     // all loads have landed (the last superstep was waited for) and no wave reads the ring
     // any more: the reduction area may overwrite it
-    uint16_t* c = G.c + (long)row0 * n;
-    if (x == 0) pk_reduce_store<NRB, 0>(acc, smem, c, n, rows, col0 + 32 * cb, wave, lane);
-    else pk_reduce_store<NRB, 1>(acc, smem, c, n, rows, col0 + 32 * cb, wave, lane);
+    pk_reduce_store<NRB>(acc, smem, G.c + (long)row0 * n, n, rows, col0, wave, lane);
     // the next tile's loads reuse the LDS just read
     barrier_lds();
 }
@@ -546,22 +542,26 @@ __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args
     (void)args_byval;
     const KernArgs& args = *(const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     const int b = blockIdx.x;
-    // (read once: the C stores of a tile could alias these as far as the compiler knows)
+    // the first tile sits at tiles[b], so its fetch does not wait for the range fetch; the
+    // range is read once (the C stores could alias it as far as the compiler knows)
     const int i_begin = args.wg_begin[b], i_end = args.wg_begin[b + 1];
-    for (int i = i_begin; i < i_end; ++i) {
+    int idx = b, next = i_begin;
+    while (true) {
         // the tile is workgroup-uniform: keep it in scalar registers so that the group
         // table is read from the kernel arguments with scalar loads
-        const TileDesc tv = args.tiles[i];
+        const TileDesc tv = args.tiles[idx];
         const TileDesc t = {__builtin_amdgcn_readfirstlane(tv.group), __builtin_amdgcn_readfirstlane(tv.row0),
                             __builtin_amdgcn_readfirstlane(tv.rows), __builtin_amdgcn_readfirstlane(tv.col0)};
         const GroupArgs& G = args.grp[t.group];
         const int n = args.n, k = args.k;
-        switch ((t.rows + 31) >> 5) {   // the planner keeps tiles within 1 .. RMAX rows
+        switch ((t.rows + 31) >> 5) {   // the planner keeps tiles within 0 .. RMAX rows
         case 1: pk_tile<1>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         case 2: pk_tile<2>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         case 3: pk_tile<3>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         default: break;
         }
+        if (next >= i_end) break;
+        idx = next++;
     }
 }
 
