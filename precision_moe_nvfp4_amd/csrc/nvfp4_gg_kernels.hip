@@ -183,6 +183,22 @@ __device__ __forceinline__ void pk_wait_loads(int n)
 #undef NVFP4GG_WAIT_CASE
 }
 
+// The same wait for the steady state of the ring, where a wave's count is one of two values
+// for a given tile height (its share of the loads times the supersteps left in flight):
+// one uniform branch instead of a search over every count.
+template <int NRB>
+__device__ __forceinline__ void pk_wait_steady(int n)
+{
+    constexpr int LO = NRB == 3 ? 4 : 6, HI = NRB == 3 ? 5 : 8;
+    if (n == HI) {
+        __builtin_amdgcn_s_waitcnt(0x0f70 | HI);   // vmcnt(HI); expcnt and lgkmcnt not waited for
+    } else if (n == LO) {
+        __builtin_amdgcn_s_waitcnt(0x0f70 | LO);
+    } else {
+        pk_wait_loads(n);
+    }
+}
+
 // Workgroup barrier for LDS hand-offs: waits for this wave's own LDS reads/writes, then
 // s_barrier.  Unlike __syncthreads() it does not wait for outstanding direct-to-LDS
 // loads (those are waited for explicitly, so later supersteps stay in flight).
@@ -337,14 +353,17 @@ __device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2],
 
 // Reduction over the four K quarters and store.  Lane (j, h) holds, in acc[c][rb] element
 // 4q + e, the partial sum of C[32 rb + j][64 cw + 32 c + 8 q + 4 h + e].  The wave with K
-// quarter t keeps element group q = t and hands the other three to the waves that keep
-// them (same column half) through LDS.
-template <int NRB>
-__device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uint8_t* smem, uint16_t* __restrict__ c0,
-                                                int n, int rows, int col, int wave, int lane)
+// quarter T keeps element group q = T and hands the other three to the waves that keep
+// them (same column half) through LDS.  T is a template parameter so that every element
+// and LDS slot index is static (no register indexing, no per-partner branches) and all
+// partner reads are in flight together.
+template <int NRB, int T>
+__device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], uint8_t* smem,
+                                                  uint16_t* __restrict__ c0, int n, int rows, int col, int wave,
+                                                  int lane)
 {
     using namespace pk;
-    const int cw = wave & 1, t = wave >> 1;
+    const int cw = wave & 1;
     u4_t* mine = reinterpret_cast<u4_t*>(smem + wave * RED_WAVE);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -352,15 +371,27 @@ __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uin
         for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (q == t) continue;
-                const int slot = q - (q > t ? 1 : 0);
+                if (q == T) continue;
+                const int slot = q - (q > T ? 1 : 0);
                 mine[((c * NRB + rb) * 3 + slot) * 64 + lane] =
                     u4_t{__float_as_uint(acc[c][rb][4 * q + 0]), __float_as_uint(acc[c][rb][4 * q + 1]),
                          __float_as_uint(acc[c][rb][4 * q + 2]), __float_as_uint(acc[c][rb][4 * q + 3])};
             }
     barrier_lds();
+    u4_t o[2][NRB][3];   // group T of the three partner waves
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+            for (int p = 0, i = 0; p < 4; ++p) {
+                if (p == T) continue;
+                const int slot = T - (T > p ? 1 : 0);   // where partner p put group T
+                o[c][rb][i++] = reinterpret_cast<const u4_t*>(smem + (cw + 2 * p) * RED_WAVE)[((c * NRB + rb) * 3 + slot) * 64 + lane];
+            }
     const int j = lane & 31, h = lane >> 5;
-    const bool vec_ok = (n & 3) == 0;
+    // the whole tile is in bounds with 8-byte aligned rows: one uniform test
+    const bool full = (n & 3) == 0 && col + BN <= n;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -368,33 +399,18 @@ __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uin
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                // acc element 4t + e; t is this wave's quarter (runtime), so pick it out
-                float a = acc[c][rb][e];
-                a = t == 1 ? acc[c][rb][4 + e] : a;
-                a = t == 2 ? acc[c][rb][8 + e] : a;
-                a = t == 3 ? acc[c][rb][12 + e] : a;
-                v[e] = a;
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                if (p == t) continue;
-                const int pw = cw + 2 * p;                      // partner wave
-                const int slot = t - (t > p ? 1 : 0);           // where the partner put group t
-                const u4_t o = reinterpret_cast<const u4_t*>(smem + pw * RED_WAVE)[((c * NRB + rb) * 3 + slot) * 64 + lane];
                 // (element-wise __uint_as_float: __builtin_bit_cast of an ext-vector element
                 // reads element 0 with this compiler)
-                v[0] += __uint_as_float(o.x);
-                v[1] += __uint_as_float(o.y);
-                v[2] += __uint_as_float(o.z);
-                v[3] += __uint_as_float(o.w);
+                v[e] = acc[c][rb][4 * T + e] + __uint_as_float(o[c][rb][0][e]) + __uint_as_float(o[c][rb][1][e]) +
+                       __uint_as_float(o[c][rb][2][e]);
             }
             const int r = rb * 32 + j;
             if (r >= rows) continue;
             const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
             const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
             uint16_t* crow = c0 + (long)r * n;
-            const int cc = col + 64 * cw + 32 * c + 8 * t + 4 * h;
-            if (vec_ok && cc + 4 <= n) {
+            const int cc = col + 64 * cw + 32 * c + 8 * T + 4 * h;
+            if (full) {
                 *reinterpret_cast<u2_t*>(crow + cc) =
                     u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
             } else {
@@ -404,6 +420,18 @@ __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uin
                 if (cc + 3 < n) crow[cc + 3] = h3;
             }
         }
+}
+
+template <int NRB>
+__device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uint8_t* smem, uint16_t* __restrict__ c0,
+                                                int n, int rows, int col, int wave, int lane)
+{
+    switch (wave >> 1) {   // the wave's K quarter (wave-uniform)
+    case 0: pk_reduce_store_q<NRB, 0>(acc, smem, c0, n, rows, col, wave, lane); break;
+    case 1: pk_reduce_store_q<NRB, 1>(acc, smem, c0, n, rows, col, wave, lane); break;
+    case 2: pk_reduce_store_q<NRB, 2>(acc, smem, c0, n, rows, col, wave, lane); break;
+    default: pk_reduce_store_q<NRB, 3>(acc, smem, c0, n, rows, col, wave, lane); break;
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -501,6 +529,8 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     }
     barrier_lds();
 
+    // loads this wave may leave in flight at the mid-superstep wait while the ring is full
+    const int wait_steady = (nslots - 2) * L.ops;
     int cs = 0;   // slot of superstep t
     for (int t = 0; t < supers; ++t) {
         // the slot of superstep t - 1 is free since the last barrier: refill it with
@@ -515,10 +545,12 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // more: harmless, and their results are unused
         const uint8_t* nxt = ring + ns * sbytes;
         pk_half<NRB, 0>(acc, bf, srow, cur, nxt, a16h[0] + aoff, a16h[1], rows, tsel, cb0, lane, tq, tid);
-        // superstep t + 1 must have landed before half 1 reads its bytes
-        if (t + 1 < supers) {
-            const int last = min(supers - 1, t - 1 + nslots);   // last superstep issued
-            pk_wait_loads((last - (t + 1)) * L.ops);
+        // superstep t + 1 must have landed before half 1 reads its bytes (loads complete in
+        // issue order, so later supersteps may stay in flight)
+        if (t + nslots - 1 < supers) {
+            pk_wait_steady<NRB>(wait_steady);   // supersteps t + 2 .. t + nslots - 1 in flight
+        } else if (t + 1 < supers) {
+            pk_wait_loads((supers - 2 - t) * L.ops);
         }
         barrier_lds();
         pk_half<NRB, 1>(acc, bf, srow, cur, nxt, a16h[1] + aoff, a16h[0], rows, tsel, cb0, lane, tq, tid);
