@@ -63,6 +63,29 @@ typedef enum {
 
 typedef struct nvfp4_gg_plan_s* nvfp4_gg_plan_t;
 
+/*
+ * Layout of the scale tensors SFA_i and SFB_i.
+ *
+ * NVFP4_GG_SCALES_ROW_MAJOR: [rows][k/16] bytes (the sfa/sfb operands of the custom_kernel
+ * docstring on the page "kernelindex submission 503584").
+ *
+ * NVFP4_GG_SCALES_BLOCKED: the pre-arranged layout the kernels on the pages consume
+ * (their sfasfb_reordered tensors).  The scales are stored in 512-byte atoms, each holding
+ * 128 rows x 4 consecutive K blocks (64 K values).  Scale (row r, K block c = kk / 16) is
+ * at byte
+ *     ((r / 128) * (k / 64) + c / 4) * 512  +  16 * (r % 32) + 4 * ((r / 32) % 4) + c % 4.
+ * The atom order (row block major, K block of 64 minor, 512 bytes each) is the scale-block
+ * address arithmetic of the B and SFA/SFB producer in "kernelindex submission 498317"; the
+ * arrangement inside an atom is the scale atom of "kernelindex submission 402102" (shape
+ * (32, 4) rows x (16, 4) K with strides (16, 4) and (0, 1)).  A tensor for `rows` rows
+ * holds nvfp4_gg_blocked_scale_bytes(rows, k) bytes: rows are padded to a multiple of 128;
+ * padding bytes are never read by nvfp4_gg_run.
+ */
+typedef enum {
+    NVFP4_GG_SCALES_ROW_MAJOR = 0,
+    NVFP4_GG_SCALES_BLOCKED = 1
+} nvfp4_gg_scale_layout_t;
+
 /* What a plan decided; filled by nvfp4_gg_plan_info. */
 typedef struct {
     int g, n, k;
@@ -76,6 +99,7 @@ typedef struct {
     int variant;           /* kernel variant id (see the design notes) */
     int order[NVFP4_GG_MAX_GROUPS];       /* group processed at schedule position p */
     int tile_begin[NVFP4_GG_MAX_GROUPS + 1]; /* exclusive tile prefix in schedule order */
+    int scale_layout;      /* nvfp4_gg_scale_layout_t the plan's runs read */
 } nvfp4_gg_plan_info_t;
 
 /*
@@ -96,6 +120,33 @@ typedef struct {
  */
 nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
                                 int device);
+
+/*
+ * nvfp4_gg_plan for scale tensors in `scale_layout` (an nvfp4_gg_scale_layout_t; any other
+ * value: NVFP4_GG_EINVAL).  nvfp4_gg_plan(...) is nvfp4_gg_plan_layout(...,
+ * NVFP4_GG_SCALES_ROW_MAJOR).  With NVFP4_GG_SCALES_BLOCKED, each SFA_i passed to
+ * nvfp4_gg_run must hold nvfp4_gg_blocked_scale_bytes(m_i, k) bytes and each SFB_i
+ * nvfp4_gg_blocked_scale_bytes(n, k) bytes; everything else is as for nvfp4_gg_run.
+ */
+nvfp4_gg_status_t nvfp4_gg_plan_layout(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
+                                       int device, int scale_layout);
+
+/* Bytes of a NVFP4_GG_SCALES_BLOCKED scale tensor with `rows` rows (0 if rows <= 0 or
+ * k is not a positive multiple of 256). */
+size_t nvfp4_gg_blocked_scale_bytes(int rows, int k);
+
+/*
+ * Enqueue on `stream` (0 = null stream of the current device) the conversion of one
+ * row-major scale tensor src[rows][k/16] into the NVFP4_GG_SCALES_BLOCKED layout at dst
+ * (nvfp4_gg_blocked_scale_bytes(rows, k) bytes, every one written; padding rows are
+ * written as zero).  Both are device pointers of the current device, 16-byte aligned
+ * (else NVFP4_GG_EALIGN), non-null for rows > 0, not overlapping (else undefined).
+ * rows = 0 does nothing.  Requirements: 0 <= rows <= 2^20, k >= 256, k % 256 == 0, else
+ * NVFP4_GG_EINVAL.  A failed launch returns NVFP4_GG_EHIP.  Asynchronous, like
+ * nvfp4_gg_run; it allocates nothing.
+ */
+nvfp4_gg_status_t nvfp4_gg_scales_to_blocked(void* dst, const void* src, int rows, int k,
+                                             hipStream_t stream);
 
 /*
  * Enqueue one grouped GEMM on `stream` (0 = the null stream of the plan's device).

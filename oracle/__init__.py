@@ -56,6 +56,13 @@ def lib():
         L.nvfp4_oracle_f16_rne.argtypes = [ctypes.c_double]
         L.nvfp4_oracle_max_threads.restype = ctypes.c_int
         L.nvfp4_oracle_grouped.restype = ctypes.c_int
+        L.nvfp4_oracle_blocked_offset.restype = ctypes.c_long
+        L.nvfp4_oracle_blocked_offset.argtypes = [ctypes.c_long, ctypes.c_long, ctypes.c_int]
+        L.nvfp4_oracle_blocked_bytes.restype = ctypes.c_long
+        L.nvfp4_oracle_blocked_bytes.argtypes = [ctypes.c_long, ctypes.c_int]
+        L.nvfp4_oracle_scales_to_blocked.restype = ctypes.c_int
+        L.nvfp4_oracle_scales_to_blocked.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_long, ctypes.c_int,
+                                                     ctypes.c_int]
         _lib = L
     return _lib
 
@@ -118,6 +125,30 @@ def grouped(m, n: int, k: int, A, B, SFA, SFB, want_exact: bool = False,
 def grouped_inputs(inp, **kw) -> OracleResult:
     """grouped() on a synthetic.GroupedInputs."""
     return grouped(inp.m, inp.n, inp.k, inp.A, inp.B, inp.SFA, inp.SFB, **kw)
+
+
+def blocked_offset(r: int, c: int, k: int) -> int:
+    """Byte offset of scale (row r, K block c) in the 128x4 blocked scale layout."""
+    return int(lib().nvfp4_oracle_blocked_offset(int(r), int(c), int(k)))
+
+
+def blocked_bytes(rows: int, k: int) -> int:
+    return int(lib().nvfp4_oracle_blocked_bytes(int(rows), int(k)))
+
+
+def scales_to_blocked(src: np.ndarray, k: int, pad: int = 0) -> np.ndarray:
+    """Row-major scales uint8 [rows, k/16] -> the blocked layout (1-D uint8); bytes of the
+    padding rows are set to `pad`."""
+    src = np.ascontiguousarray(src, dtype=np.uint8)
+    rows = src.shape[0]
+    if src.shape != (rows, k // 16):
+        raise ValueError("scale matrix must be [rows, k/16]")
+    dst = np.empty(blocked_bytes(rows, k), dtype=np.uint8)
+    rc = lib().nvfp4_oracle_scales_to_blocked(dst.ctypes.data if dst.size else None,
+                                              src.ctypes.data if src.size else None, rows, k, pad)
+    if rc != 0:
+        raise RuntimeError("oracle blocked conversion failed")
+    return dst
 
 
 def ulp16(ref_bits: np.ndarray) -> np.ndarray:

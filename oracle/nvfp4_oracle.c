@@ -27,7 +27,9 @@
  *   - E2M1 is the OCP Microscaling FP4 format (bias 1, no Inf/NaN).
  *   - E4M3FN is the OCP FP8 E4M3 format (bias 7, S.1111.111 is NaN, max 448).
  *   - Packing: two E2M1 codes per byte along K, low nibble = even K index.
- *   - Scales are row-major [rows][k/16].
+ *   - Scales are row-major [rows][k/16] (the plain definition); the 128x4 blocked
+ *     scale layout is an index permutation of it, written out in
+ *     nvfp4_oracle_blocked_offset below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -160,4 +162,44 @@ int nvfp4_oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/*
+ * 128x4 blocked scale layout: byte offset of scale (row r, K block c = kk / 16) of a
+ * scale matrix for K = k.
+ *   - Atoms of 512 bytes are ordered row block (128 rows) major, K block of 64 values
+ *     (4 scales) minor: atom (r / 128) * (k / 64) + c / 4.  This is the address of the
+ *     SFA/SFB scale blocks in the producer branch of the kernel on the page "kernelindex
+ *     submission 498317" (row offset / 128 times K / 16 / 4, plus K offset / 64, times 512).
+ *   - Inside an atom, the row splits into (r % 32, (r / 32) % 4) with byte strides (16, 4)
+ *     and the scale into (c % 4) with stride 1: the scale atom of the page "kernelindex
+ *     submission 402102" (shape ((32, 4), (16, 4)), stride ((16, 4), (0, 1)), where the
+ *     16 K values sharing a scale have stride 0).
+ */
+long nvfp4_oracle_blocked_offset(long r, long c, int k)
+{
+    const long atom = (r / 128) * (long)(k / 64) + c / 4;
+    return atom * 512 + 16 * (r % 32) + 4 * ((r / 32) % 4) + (c % 4);
+}
+
+/* Bytes of the blocked layout for `rows` rows: whole 128-row blocks of k / 64 atoms. */
+long nvfp4_oracle_blocked_bytes(long rows, int k)
+{
+    return rows <= 0 ? 0 : ((rows + 127) / 128) * (long)(k / 64) * 512;
+}
+
+/*
+ * src [rows][k/16] row-major -> dst in the blocked layout; dst bytes that no (r, c) maps
+ * to (the rows of the last block beyond `rows`) are set to `pad`.  Returns 0, or -1 on an
+ * argument error (k must be a positive multiple of 64).
+ */
+int nvfp4_oracle_scales_to_blocked(uint8_t* dst, const uint8_t* src, long rows, int k, int pad)
+{
+    if (rows < 0 || k <= 0 || (k % 64) != 0 || (rows > 0 && (!dst || !src))) return -1;
+    if (rows == 0) return 0;
+    memset(dst, pad & 0xFF, (size_t)nvfp4_oracle_blocked_bytes(rows, k));
+    const long cols = k / 16;
+    for (long r = 0; r < rows; ++r)
+        for (long c = 0; c < cols; ++c) dst[nvfp4_oracle_blocked_offset(r, c, k)] = src[r * cols + c];
+    return 0;
 }

@@ -5,7 +5,9 @@ libnvfp4gg.so.  There is no fallback: if the library is missing, importing the b
 raises.  PyTorch is used for device memory and streams only.
 
 Names mirror the C ABI:
-    plan = nvfp4_gg_plan(m, n, k, device=-1)
+    plan = nvfp4_gg_plan(m, n, k, device=-1, scale_layout=SCALES_ROW_MAJOR)
+    nvfp4_gg_blocked_scale_bytes(rows, k)
+    nvfp4_gg_scales_to_blocked(dst, src, rows, k, stream=None)
     nvfp4_gg_run(plan, A, B, SFA, SFB, C, stream=None)
     info = nvfp4_gg_plan_info(plan)
     nvfp4_gg_destroy(plan)
@@ -27,6 +29,7 @@ MAX_GROUPS = 64
 DEVICE_NONE = -2
 
 OK, EINVAL, EALIGN, ENOMEM, EHIP, EUNSUPPORTED = range(6)
+SCALES_ROW_MAJOR, SCALES_BLOCKED = 0, 1
 
 
 class Nvfp4GGError(RuntimeError):
@@ -44,6 +47,7 @@ class PlanInfo(ctypes.Structure):
         ("lds_bytes", ctypes.c_int), ("variant", ctypes.c_int),
         ("order", ctypes.c_int * MAX_GROUPS),
         ("tile_begin", ctypes.c_int * (MAX_GROUPS + 1)),
+        ("scale_layout", ctypes.c_int),
     ]
 
 
@@ -73,6 +77,13 @@ def _load():
     L.nvfp4_gg_plan.restype = ctypes.c_int
     L.nvfp4_gg_plan.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.nvfp4_gg_plan_layout.restype = ctypes.c_int
+    L.nvfp4_gg_plan_layout.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.nvfp4_gg_blocked_scale_bytes.restype = ctypes.c_size_t
+    L.nvfp4_gg_blocked_scale_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.nvfp4_gg_scales_to_blocked.restype = ctypes.c_int
+    L.nvfp4_gg_scales_to_blocked.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
     L.nvfp4_gg_run.restype = ctypes.c_int
     L.nvfp4_gg_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.nvfp4_gg_plan_info.restype = ctypes.c_int
@@ -148,14 +159,29 @@ def nvfp4_gg_status_string(status: int) -> str:
     return _lib.nvfp4_gg_status_string(int(status)).decode()
 
 
-def nvfp4_gg_plan(m: Sequence[int], n: int, k: int, device: int = -1) -> Plan:
+def nvfp4_gg_plan(m: Sequence[int], n: int, k: int, device: int = -1,
+                  scale_layout: int = SCALES_ROW_MAJOR) -> Plan:
     g = len(m)
     out = ctypes.c_void_p()
     marr = (ctypes.c_int * max(g, 1))(*[int(x) for x in m])
-    st = _lib.nvfp4_gg_plan(ctypes.byref(out), g, marr if g else None, int(n), int(k), int(device))
+    st = _lib.nvfp4_gg_plan_layout(ctypes.byref(out), g, marr if g else None, int(n), int(k), int(device),
+                                   int(scale_layout))
     if st != OK:
-        raise Nvfp4GGError(st, "nvfp4_gg_plan")
+        raise Nvfp4GGError(st, "nvfp4_gg_plan_layout")
     return Plan(out.value, m, int(n), int(k))
+
+
+def nvfp4_gg_blocked_scale_bytes(rows: int, k: int) -> int:
+    return int(_lib.nvfp4_gg_blocked_scale_bytes(int(rows), int(k)))
+
+
+def nvfp4_gg_scales_to_blocked(dst, src, rows: int, k: int, stream=None) -> None:
+    """Enqueue the row-major -> 128x4 blocked conversion of one scale tensor (device
+    tensors or addresses; dst holds nvfp4_gg_blocked_scale_bytes(rows, k) bytes)."""
+    st = _lib.nvfp4_gg_scales_to_blocked(ctypes.c_void_p(_addr(dst)), ctypes.c_void_p(_addr(src)), int(rows),
+                                         int(k), ctypes.c_void_p(_stream_handle(stream)))
+    if st != OK:
+        raise Nvfp4GGError(st, "nvfp4_gg_scales_to_blocked")
 
 
 def nvfp4_gg_run(plan: Plan, A=None, B=None, SFA=None, SFB=None, C=None, stream=None,

@@ -33,6 +33,7 @@ struct nvfp4_gg_plan_s {
     int device;
     int num_cus;
     int variant;
+    int scale_layout;            // nvfp4_gg_scale_layout_t
     VariantShape shape;
     int chunk_rows;              // chosen maximum rows per tile
     int total_tiles;
@@ -178,8 +179,15 @@ static void free_device(nvfp4_gg_plan_s* p)
 
 extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k, int device)
 {
+    return nvfp4_gg_plan_layout(out, g, m, n, k, device, NVFP4_GG_SCALES_ROW_MAJOR);
+}
+
+extern "C" nvfp4_gg_status_t nvfp4_gg_plan_layout(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
+                                                  int device, int scale_layout)
+{
     if (out == nullptr) return NVFP4_GG_EINVAL;
     *out = nullptr;
+    if (scale_layout != NVFP4_GG_SCALES_ROW_MAJOR && scale_layout != NVFP4_GG_SCALES_BLOCKED) return NVFP4_GG_EINVAL;
     if (m == nullptr || g < 1 || n < 1 || k < 256 || (k % 256) != 0) return NVFP4_GG_EINVAL;
     if (g > NVFP4_GG_MAX_GROUPS) return NVFP4_GG_EUNSUPPORTED;
     for (int i = 0; i < g; ++i)
@@ -204,7 +212,8 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const in
         p->k = k;
         p->device = device;
         p->num_cus = num_cus;
-        p->variant = kVariantPersistent;
+        p->scale_layout = scale_layout;
+        p->variant = scale_layout == NVFP4_GG_SCALES_BLOCKED ? kVariantPersistentBlocked : kVariantPersistent;
         p->shape = variant_shape(p->variant);
         p->m.assign(m, m + g);
 
@@ -344,6 +353,24 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_p
     info->variant = plan->variant;
     for (int s = 0; s < plan->g; ++s) info->order[s] = plan->order[s];
     for (int s = 0; s <= plan->g; ++s) info->tile_begin[s] = plan->tile_begin[s];
+    info->scale_layout = plan->scale_layout;
+    return NVFP4_GG_OK;
+}
+
+extern "C" size_t nvfp4_gg_blocked_scale_bytes(int rows, int k)
+{
+    if (rows <= 0 || k < 256 || (k % 256) != 0) return 0;
+    return (size_t)blocked_scale_bytes(rows, k);
+}
+
+extern "C" nvfp4_gg_status_t nvfp4_gg_scales_to_blocked(void* dst, const void* src, int rows, int k,
+                                                        hipStream_t stream)
+{
+    if (rows < 0 || rows > kMaxRows || k < 256 || (k % 256) != 0) return NVFP4_GG_EINVAL;
+    if (rows == 0) return NVFP4_GG_OK;
+    if (dst == nullptr || src == nullptr) return NVFP4_GG_EINVAL;
+    if (!aligned16(dst) || !aligned16(src)) return NVFP4_GG_EALIGN;
+    if (launch_scales_to_blocked(dst, src, rows, k, stream) != hipSuccess) return NVFP4_GG_EHIP;
     return NVFP4_GG_OK;
 }
 

@@ -48,12 +48,22 @@ struct VariantShape {
 };
 
 enum Variant : int {
-    kVariantPersistent = 2,  // persistent 8-wave workgroups over a planned tile list
+    kVariantPersistent = 2,         // persistent 8-wave workgroups over a planned tile list
+    kVariantPersistentBlocked = 3,  // the same, reading 128x4 blocked scale tensors
 };
 
 VariantShape variant_shape(int variant);
 
 // Enqueue one launch of `variant` with `grid` workgroups.
 hipError_t launch_variant(int variant, const KernArgs& args, int grid, hipStream_t stream);
+
+// Bytes of a 128x4 blocked scale tensor: ceil(rows / 128) row blocks of k / 64 atoms of 512 B.
+inline long blocked_scale_bytes(int rows, int k)
+{
+    return rows <= 0 ? 0 : (long)((rows + 127) / 128) * (k / 64) * 512;
+}
+
+// Enqueue the row-major -> blocked scale conversion (padding rows written as zero).
+hipError_t launch_scales_to_blocked(void* dst, const void* src, int rows, int k, hipStream_t stream);
 
 }  // namespace nvfp4gg

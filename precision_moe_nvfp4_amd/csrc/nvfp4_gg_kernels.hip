@@ -134,14 +134,17 @@ static_assert(8 * RED_WAVE <= LDS_BYTES, "reduction area must fit in LDS");
 // ---------------------------------------------------------------------------------------
 
 // Per-wave direct-to-LDS loads of one superstep.  B code instruction i (rows 8i .. +8,
-// i < 16) goes to wave i % 8, B scale instruction q (rows 32q .. +32, lanes < 32) to
-// wave q; A code instruction a (rows 8a .. +8) to wave (a + 4) % 8, A scale instruction q
-// to wave 7 - q.
+// i < 16) goes to wave i % 8 and A code instruction a (rows 8a .. +8) to wave (a + 4) % 8.
+// Scales, row-major layout: B scale instruction q (rows 32q .. +32, 16 bytes per lane,
+// lanes < 32) to wave q < 4, A scale instruction q to wave 7 - q.  Scales, 128x4 blocked
+// layout: 4 bytes per lane, so instruction q covers rows 16q .. +16; B scale instruction q
+// to wave q (all 8), A scale instruction q to wave q.  Either way the LDS copy of a
+// superstep's scales is the same: row r's 16 bytes at 16 r.
 struct SuperLoads {
     const uint8_t* b[2];  // B codes of this lane, superstep 0
-    const uint8_t* sb;    // B scales of this lane (lanes < 32)
+    const uint8_t* sb;    // B scales of this lane
     const uint8_t* a[2];  // A codes of this lane
-    const uint8_t* sa;    // A scales of this lane (lanes < 32)
+    const uint8_t* sa;    // A scales of this lane
     int b_dst[2];         // LDS offsets (inside a slot) of the B code instructions
     int sb_dst;
     int a_dst[2];
@@ -152,16 +155,47 @@ struct SuperLoads {
     int ops;              // loads per superstep issued by this wave
 };
 
+// Loads per superstep issued by wave w for tiles of 32 nrb rows (the assignment above).
+__host__ __device__ constexpr int pk_ops(int w, int nrb, bool blocked)
+{
+    int ops = 2;                                            // B codes: instructions w, w + 8
+    ops += blocked ? 1 : (w < 4 ? 1 : 0);                   // B scales
+    for (int q = 0; q < 2; ++q) ops += ((w + 4) & 7) + 8 * q < 4 * nrb ? 1 : 0;   // A codes
+    ops += blocked ? (w < 2 * nrb ? 1 : 0) : (7 - w < nrb ? 1 : 0);             // A scales
+    return ops;
+}
+__host__ __device__ constexpr int pk_ops_min(int nrb, bool blocked)
+{
+    int v = pk_ops(0, nrb, blocked);
+    for (int w = 1; w < 8; ++w) v = pk_ops(w, nrb, blocked) < v ? pk_ops(w, nrb, blocked) : v;
+    return v;
+}
+__host__ __device__ constexpr int pk_ops_max(int nrb, bool blocked)
+{
+    int v = pk_ops(0, nrb, blocked);
+    for (int w = 1; w < 8; ++w) v = pk_ops(w, nrb, blocked) > v ? pk_ops(w, nrb, blocked) : v;
+    return v;
+}
+
+template <bool BLK>
 __device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, const SuperLoads& L, int lane)
 {
     using namespace pk;
-    const long kb = (long)t * ROWB, ks = (long)t * SCB;
+    const long kb = (long)t * ROWB;
     __builtin_amdgcn_global_load_lds(L.b[0] + kb, slot_base + L.b_dst[0], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(L.b[1] + kb, slot_base + L.b_dst[1], 16, 0, 0);
-    if (L.nsb > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 16, 0, 0);
+    if constexpr (BLK) {
+        // four 512-byte atoms (4 scales x 128 rows each) per superstep
+        const long ks = (long)t * (4 * 512);
+        if (L.nsb > 0) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 4, 0, 0);
+        if (L.nsa > 0) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 4, 0, 0);
+    } else {
+        const long ks = (long)t * SCB;
+        if (L.nsb > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 16, 0, 0);
+        if (L.nsa > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 16, 0, 0);
+    }
     if (L.na > 0) __builtin_amdgcn_global_load_lds(L.a[0] + kb, slot_base + L.a_dst[0], 16, 0, 0);
     if (L.na > 1) __builtin_amdgcn_global_load_lds(L.a[1] + kb, slot_base + L.a_dst[1], 16, 0, 0);
-    if (L.nsa > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 16, 0, 0);
 }
 
 // Wait until at most n of this wave's loads are in flight (0 <= n <= 30).
@@ -184,12 +218,14 @@ __device__ __forceinline__ void pk_wait_loads(int n)
 }
 
 // The same wait for the steady state of the ring, where a wave's count is one of two values
-// for a given tile height (its share of the loads times the supersteps left in flight):
-// one uniform branch instead of a search over every count.
-template <int NRB>
+// for a given tile height and scale layout (its share of the loads times the supersteps
+// left in flight): one uniform branch instead of a search over every count.
+template <int NRB, bool BLK>
 __device__ __forceinline__ void pk_wait_steady(int n)
 {
-    constexpr int LO = NRB == 3 ? 4 : 6, HI = NRB == 3 ? 5 : 8;
+    constexpr int AHEAD = pk::ring_slots(32 * NRB) - 2;
+    constexpr int LO = AHEAD * pk_ops_min(NRB, BLK), HI = AHEAD * pk_ops_max(NRB, BLK);
+    static_assert(HI <= 15, "the constant waits use the 4 low vmcnt bits");
     if (n == HI) {
         __builtin_amdgcn_s_waitcnt(0x0f70 | HI);   // vmcnt(HI); expcnt and lgkmcnt not waited for
     } else if (n == LO) {
@@ -440,8 +476,8 @@ __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uin
 
 // One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)).  All
 // 8 waves execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs
-// per B fragment.
-template <int NRB>
+// per B fragment; BLK selects the 128x4 blocked scale layout (else row-major scales).
+template <int NRB, bool BLK>
 __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_, uint8_t* smem)
 {
     using namespace pk;
@@ -474,10 +510,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             L.b[q] = G.b + (long)min(col0 + r, n - 1) * qs + 16 * (pos ^ swz(r));
             L.b_dst[q] = 8 * i * ROWB;
         }
-        L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
-        L.sb = G.sfb + (long)min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) * ss;
-        L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
-        const int na_total = rpad / 8, nsa_total = rpad / 32;
+        const int na_total = rpad / 8;
         L.na = 0;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -487,10 +520,31 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
             if (a < na_total) L.na = q + 1;
         }
-        const int qa = 7 - wave;         // A scale instruction
-        L.nsa = qa < nsa_total ? 1 : 0;
-        L.sa = G.sfa + (long)(row0 + min(32 * qa + (lane & 31), rows - 1)) * ss;
-        L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
+        if constexpr (BLK) {
+            // 128x4 blocked scales: the scale of (row r, K block c) sits in 512-byte atom
+            // (r / 128) * (k / 64) + c / 4 at byte 16 (r % 32) + 4 ((r / 32) % 4) + c % 4, so
+            // the 4 scales of a row in one atom are contiguous.  Lane l of scale instruction
+            // q = wave loads the 4 bytes of row 16 q + l / 4 in the superstep's atom l % 4
+            // (K blocks 16 t + 4 (l % 4) .. +4), which land at LDS byte 16 (row) + 4 (l % 4).
+            const long atoms = k / 64;
+            const int piece = lane & 3;
+            const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
+            L.nsb = 1;
+            L.sb = G.sfb + ((long)(gb >> 7) * atoms + piece) * 512 + 16 * (gb & 31) + 4 * ((gb >> 5) & 3);
+            L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
+            const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
+            L.nsa = wave < rpad / 16 ? 1 : 0;
+            L.sa = G.sfa + ((long)(ga >> 7) * atoms + piece) * 512 + 16 * (ga & 31) + 4 * ((ga >> 5) & 3);
+            L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
+        } else {
+            L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
+            L.sb = G.sfb + (long)min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) * ss;
+            L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
+            const int qa = 7 - wave;         // A scale instruction
+            L.nsa = qa < rpad / 32 ? 1 : 0;
+            L.sa = G.sfa + (long)(row0 + min(32 * qa + (lane & 31), rows - 1)) * ss;
+            L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
+        }
         L.ops = 2 + L.nsb + L.na + L.nsa;
     }
 
@@ -505,9 +559,9 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     // 1 .. nslots-1; dequantise the A of superstep 0's first half and read the raw B
     // operand of its first step
     const int first = min(nslots, supers);
-    pk_issue(ring, 0, L, lane);
+    pk_issue<BLK>(ring, 0, L, lane);
     pk_wait_loads(0);
-    for (int t = 1; t < first; ++t) pk_issue(ring + t * sbytes, t, L, lane);
+    for (int t = 1; t < first; ++t) pk_issue<BLK>(ring + t * sbytes, t, L, lane);
     barrier_lds();
     uint8_t* a16h[2] = {a16, a16 + rpad * A_ROW};
     const int aoff = j * A_ROW + 128 * h + 32 * tq;   // this lane's A fragment row
@@ -537,7 +591,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // superstep t - 1 + nslots
         if (t > 0 && t - 1 + nslots < supers) {
             const int fs = (cs == 0) ? nslots - 1 : cs - 1;
-            pk_issue(ring + fs * sbytes, t - 1 + nslots, L, lane);
+            pk_issue<BLK>(ring + fs * sbytes, t - 1 + nslots, L, lane);
         }
         const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
         const uint8_t* cur = ring + cs * sbytes;
@@ -548,7 +602,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // superstep t + 1 must have landed before half 1 reads its bytes (loads complete in
         // issue order, so later supersteps may stay in flight)
         if (t + nslots - 1 < supers) {
-            pk_wait_steady<NRB>(wait_steady);   // supersteps t + 2 .. t + nslots - 1 in flight
+            pk_wait_steady<NRB, BLK>(wait_steady);   // supersteps t + 2 .. t + nslots - 1 in flight
         } else if (t + 1 < supers) {
             pk_wait_loads((supers - 2 - t) * L.ops);
         }
@@ -565,13 +619,13 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     barrier_lds();
 }
 
-// Persistent kernel: workgroup b processes tiles list[begin[b] .. begin[b+1]) in order.
-__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args_byval)
+// Persistent kernel body: workgroup b processes its first tile tiles[b], then tiles
+// list[begin[b] .. begin[b+1]) in order.
+template <bool BLK>
+__device__ __forceinline__ void pk_persistent(uint8_t* smem)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
     // index the group table in place in the kernarg segment (scalar loads), rather than
     // through the by-value copy
-    (void)args_byval;
     const KernArgs& args = *(const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     const int b = blockIdx.x;
     // the first tile sits at tiles[b], so its fetch does not wait for the range fetch; the
@@ -587,9 +641,9 @@ __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args
         const GroupArgs& G = args.grp[t.group];
         const int n = args.n, k = args.k;
         switch ((t.rows + 31) >> 5) {   // the planner keeps tiles within 0 .. RMAX rows
-        case 1: pk_tile<1>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 2: pk_tile<2>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 3: pk_tile<3>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+        case 1: pk_tile<1, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+        case 2: pk_tile<2, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+        case 3: pk_tile<3, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         default: break;
         }
         if (next >= i_end) break;
@@ -597,10 +651,27 @@ __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args
     }
 }
 
+// Row-major scales ([rows][k/16]).
+__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args_byval)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
+    (void)args_byval;
+    pk_persistent<false>(smem);
+}
+
+// 128x4 blocked scales (512-byte atoms).
+__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent_blocked(KernArgs args_byval)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
+    (void)args_byval;
+    pk_persistent<true>(smem);
+}
+
 VariantShape variant_shape(int variant)
 {
     switch (variant) {
     case kVariantPersistent:
+    case kVariantPersistentBlocked:
         return VariantShape{pk::RMAX, pk::BN, pk::THREADS, pk::LDS_BYTES};
     default:
         return VariantShape{0, 0, 0, 0};
@@ -610,16 +681,55 @@ VariantShape variant_shape(int variant)
 hipError_t launch_variant(int variant, const KernArgs& args, int grid, hipStream_t stream)
 {
     if (grid <= 0) return hipSuccess;
+    KernArgs a = args;
+    void* params[] = {&a};
     switch (variant) {
-    case kVariantPersistent: {
-        KernArgs a = args;
-        void* params[] = {&a};
+    case kVariantPersistent:
         return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent), dim3(grid), dim3(pk::THREADS),
                                params, 0, stream);
-    }
+    case kVariantPersistentBlocked:
+        return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent_blocked), dim3(grid),
+                               dim3(pk::THREADS), params, 0, stream);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+// ---------------------------------------------------------------------------------------
+// Scale layout conversion
+// ---------------------------------------------------------------------------------------
+
+// Row-major scales [rows][k/16] -> 128x4 blocked layout.  One thread per output dword:
+// dword w of atom a holds the 4 scales of row 128 (a / (k/64)) + 32 (w % 4) + w / 4 in
+// K blocks 4 (a % (k/64)) .. +4, which are one aligned dword of that source row.  Rows
+// at or beyond `rows` (the padding of the last 128-row block) are written as zero.
+__global__ __launch_bounds__(256) void nvfp4_gg_scales_to_blocked_kernel(uint32_t* __restrict__ dst,
+                                                                         const uint8_t* __restrict__ src, int rows,
+                                                                         int k, long ndw)
+{
+    const long d = (long)blockIdx.x * 256 + threadIdx.x;
+    if (d >= ndw) return;
+    const long atoms = k / 64;
+    const long a = d >> 7;
+    const int w = (int)(d & 127);
+    const long row = (a / atoms) * 128 + 32 * (w & 3) + (w >> 2);
+    const long c4 = a % atoms;
+    uint32_t v = 0;
+    if (row < rows) v = *reinterpret_cast<const uint32_t*>(src + row * (k / 16) + 4 * c4);
+    dst[d] = v;
+}
+
+hipError_t launch_scales_to_blocked(void* dst, const void* src, int rows, int k, hipStream_t stream)
+{
+    const long ndw = blocked_scale_bytes(rows, k) / 4;
+    if (ndw == 0) return hipSuccess;
+    const long grid = (ndw + 255) / 256;
+    void* d = dst;
+    const void* s_ = src;
+    long nd = ndw;
+    void* params[] = {&d, &s_, &rows, &k, &nd};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_scales_to_blocked_kernel), dim3((unsigned)grid),
+                           dim3(256), params, 0, stream);
 }
 
 }  // namespace nvfp4gg

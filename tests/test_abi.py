@@ -15,12 +15,13 @@ HEADER = os.path.join(ROOT, "include", "nvfp4_gg.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"^\s*(?:nvfp4_gg_status_t|void|const char\s*\*)\s*(nvfp4_gg_\w+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:nvfp4_gg_status_t|void|size_t|const char\s*\*)\s*(nvfp4_gg_\w+)\s*\(", text, re.M)
 
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {
-        "nvfp4_gg_plan", "nvfp4_gg_run", "nvfp4_gg_plan_info", "nvfp4_gg_destroy", "nvfp4_gg_status_string"}
+        "nvfp4_gg_plan", "nvfp4_gg_plan_layout", "nvfp4_gg_run", "nvfp4_gg_plan_info", "nvfp4_gg_destroy",
+        "nvfp4_gg_status_string", "nvfp4_gg_blocked_scale_bytes", "nvfp4_gg_scales_to_blocked"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -118,3 +119,36 @@ def test_run_validates_pointers_before_touching_the_device():
 def test_plan_info_rejects_null():
     L = gg.library()
     assert L.nvfp4_gg_plan_info(None, None) == gg.EINVAL
+
+
+def test_plan_layout_validation_and_info():
+    L = gg.library()
+    out = ctypes.c_void_p(1234)
+    marr = (ctypes.c_int * 2)(100, 3)
+    assert L.nvfp4_gg_plan_layout(ctypes.byref(out), 2, marr, 64, 256, gg.DEVICE_NONE, 2) == gg.EINVAL
+    assert out.value is None
+    assert L.nvfp4_gg_plan_layout(ctypes.byref(out), 2, marr, 64, 256, gg.DEVICE_NONE, -1) == gg.EINVAL
+    for layout in (gg.SCALES_ROW_MAJOR, gg.SCALES_BLOCKED):
+        plan = gg.nvfp4_gg_plan([100, 3], 64, 256, device=gg.DEVICE_NONE, scale_layout=layout)
+        info = gg.nvfp4_gg_plan_info(plan)
+        assert info.scale_layout == layout
+        assert info.variant == (3 if layout == gg.SCALES_BLOCKED else 2)
+        assert info.total_tiles > 0
+
+
+@pytest.mark.parametrize("rows,k,expect", [
+    (1, 256, 2048), (128, 256, 2048), (129, 256, 4096), (300, 1536, 3 * 24 * 512), (0, 256, 0), (-1, 256, 0),
+    (10, 128, 0), (10, 300, 0),
+])
+def test_blocked_scale_bytes(rows, k, expect):
+    assert gg.nvfp4_gg_blocked_scale_bytes(rows, k) == expect
+
+
+def test_scales_to_blocked_validates_before_touching_the_device():
+    L = gg.library()
+    vp = ctypes.c_void_p
+    assert L.nvfp4_gg_scales_to_blocked(vp(16), vp(32), 10, 300, None) == gg.EINVAL
+    assert L.nvfp4_gg_scales_to_blocked(vp(16), vp(32), -1, 256, None) == gg.EINVAL
+    assert L.nvfp4_gg_scales_to_blocked(None, vp(32), 10, 256, None) == gg.EINVAL
+    assert L.nvfp4_gg_scales_to_blocked(vp(16), vp(36), 10, 256, None) == gg.EALIGN
+    assert L.nvfp4_gg_scales_to_blocked(None, None, 0, 256, None) == gg.OK
