@@ -99,13 +99,29 @@ def make_sets(torch, gg, name, R, dev):
     return cfg, sets, Cs
 
 
-def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False):
+def to_blocked(torch, gg, scales, k, dev):
+    """Row-major scale tensors -> 128x4 blocked copies, converted by the library."""
+    out = []
+    for s in scales:
+        rows = s.shape[0]
+        d = torch.empty((max(gg.nvfp4_gg_blocked_scale_bytes(rows, k), 1),), dtype=torch.uint8, device=dev)
+        gg.nvfp4_gg_scales_to_blocked(d, s, rows, k)
+        out.append(d)
+    return out
+
+
+def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=False):
     cfg = shape_of(name)
     nbytes = algorithmic_bytes(cfg.m, cfg.n, cfg.k)
     flops = algorithmic_flops(cfg.m, cfg.n, cfg.k)
     R = max(1, math.ceil(COLD_BYTES / nbytes))
     cfg, sets, Cs = make_sets(torch, gg, name, R, dev)
-    plan = gg.nvfp4_gg_plan(cfg.m, cfg.n, cfg.k)
+    if blocked:
+        # the same scale values in the 128x4 blocked layout (converted before timing)
+        sets = [(A, B, to_blocked(torch, gg, SFA, cfg.k, dev), to_blocked(torch, gg, SFB, cfg.k, dev))
+                for (A, B, SFA, SFB) in sets]
+        torch.cuda.synchronize()
+    plan = gg.nvfp4_gg_plan(cfg.m, cfg.n, cfg.k, scale_layout=gg.SCALES_BLOCKED if blocked else gg.SCALES_ROW_MAJOR)
     info = gg.nvfp4_gg_plan_info(plan)
     args = [gg.RunArgs(len(cfg.m), *sets[r], Cs[r]) for r in range(R)]
     stream = torch.cuda.Stream()
@@ -164,6 +180,7 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False):
         "bound": "mfma" if flops / (PEAK_F16_TFLOPS * 1e6) >= nbytes / (PEAK_HBM_GBS * 1e3) else "hbm",
         "rotating_sets": R,
         "grid": info.grid, "block": info.block, "tile": [info.tile_m, info.tile_n],
+        "scale_layout": "blocked128x4" if blocked else "row-major",
         "page_b200_us": PAGE_US.get(name),
     }
     del sets, Cs, args
@@ -241,6 +258,13 @@ def main():
     for nm in names:
         print(f"bench: timing {nm} {shape_of(nm)}", file=sys.stderr, flush=True)
         shapes[nm] = time_shape(torch, gg, nm, a.steps, a.warmup, dev, cold_only=a.cold_only)
+        print(f"bench: {nm} -> {shapes[nm]}", file=sys.stderr, flush=True)
+    if not a.cold_only:
+        # the headline workload again with its scales in the 128x4 blocked layout
+        nm = HEADLINE + "_blocked_scales"
+        print(f"bench: timing {nm}", file=sys.stderr, flush=True)
+        shapes[nm] = time_shape(torch, gg, HEADLINE, a.steps, a.warmup, dev, cold_only=True, blocked=True)
+        shapes[nm]["page_b200_us"] = None
         print(f"bench: {nm} -> {shapes[nm]}", file=sys.stderr, flush=True)
     head = shapes[HEADLINE]
     cfg = CONFIGS[HEADLINE]
