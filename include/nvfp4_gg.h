@@ -86,9 +86,23 @@ typedef enum {
     NVFP4_GG_SCALES_BLOCKED = 1
 } nvfp4_gg_scale_layout_t;
 
+/*
+ * One problem of a grouped call with its own sizes (nvfp4_gg_plan_problems): the custom_kernel
+ * of "kernelindex submission 503584" takes one (m, n, k, l) per group, and its kernel
+ * addresses C through per-group strides.
+ *   m   rows of A_i and C_i (0 <= m <= 2^20; 0: nothing is read or written for the group)
+ *   n   rows of B_i and columns of C_i (1 <= n <= 2^20)
+ *   k   K of the group (256 <= k <= 2^20, k % 256 == 0)
+ *   ldc elements between the starts of consecutive rows of C_i: 0 means n, otherwise >= n;
+ *       the elements of a row beyond column n are never written
+ */
+typedef struct {
+    int m, n, k, ldc;
+} nvfp4_gg_problem_t;
+
 /* What a plan decided; filled by nvfp4_gg_plan_info. */
 typedef struct {
-    int g, n, k;
+    int g, n, k;           /* n and k shared by every group, or 0 where they differ */
     int device;            /* HIP device ordinal, or NVFP4_GG_DEVICE_NONE */
     int num_cus;           /* compute units the schedule was sized for */
     int tile_m, tile_n;    /* largest output tile of one workgroup (rows, columns) */
@@ -130,6 +144,18 @@ nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n
  */
 nvfp4_gg_status_t nvfp4_gg_plan_layout(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
                                        int device, int scale_layout);
+
+/*
+ * The general plan: group i has its own sizes problems[i] (host array of g, copied; see
+ * nvfp4_gg_problem_t for the limits, NVFP4_GG_EINVAL outside them) and the operand shapes
+ * of group i are A_i [m][k/2], B_i [n][k/2], SFA_i [m][k/16] and SFB_i [n][k/16] (or their
+ * blocked-layout sizes for NVFP4_GG_SCALES_BLOCKED), C_i rows of ldc (or n) fp16 elements.
+ * Everything else is as nvfp4_gg_plan_layout; nvfp4_gg_plan_layout(out, g, m, n, k, device,
+ * layout) is this call with problems[i] = {m[i], n, k, 0}.  With a nonzero ldc the row starts
+ * of C_i must stay 2-byte aligned; 8-byte stores are used when ldc % 4 == 0.
+ */
+nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g, const nvfp4_gg_problem_t* problems,
+                                         int device, int scale_layout);
 
 /* Bytes of a NVFP4_GG_SCALES_BLOCKED scale tensor with `rows` rows (0 if rows <= 0 or
  * k is not a positive multiple of 256). */

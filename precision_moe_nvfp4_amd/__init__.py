@@ -6,6 +6,7 @@ raises.  PyTorch is used for device memory and streams only.
 
 Names mirror the C ABI:
     plan = nvfp4_gg_plan(m, n, k, device=-1, scale_layout=SCALES_ROW_MAJOR)
+    plan = nvfp4_gg_plan_problems([(m_i, n_i, k_i, ldc_i), ...], device=-1, scale_layout=...)
     nvfp4_gg_blocked_scale_bytes(rows, k)
     nvfp4_gg_scales_to_blocked(dst, src, rows, k, stream=None)
     nvfp4_gg_run(plan, A, B, SFA, SFB, C, stream=None)
@@ -36,6 +37,10 @@ class Nvfp4GGError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
         super().__init__(f"{what}: {nvfp4_gg_status_string(status)} (status {status})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int), ("n", ctypes.c_int), ("k", ctypes.c_int), ("ldc", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -80,6 +85,9 @@ def _load():
     L.nvfp4_gg_plan_layout.restype = ctypes.c_int
     L.nvfp4_gg_plan_layout.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.nvfp4_gg_plan_problems.restype = ctypes.c_int
+    L.nvfp4_gg_plan_problems.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(Problem), ctypes.c_int,
+                                         ctypes.c_int]
     L.nvfp4_gg_blocked_scale_bytes.restype = ctypes.c_size_t
     L.nvfp4_gg_blocked_scale_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
     L.nvfp4_gg_scales_to_blocked.restype = ctypes.c_int
@@ -169,6 +177,22 @@ def nvfp4_gg_plan(m: Sequence[int], n: int, k: int, device: int = -1,
     if st != OK:
         raise Nvfp4GGError(st, "nvfp4_gg_plan_layout")
     return Plan(out.value, m, int(n), int(k))
+
+
+def nvfp4_gg_plan_problems(problems, device: int = -1, scale_layout: int = SCALES_ROW_MAJOR) -> Plan:
+    """problems: sequence of (m, n, k) or (m, n, k, ldc) per group (ldc 0 = n)."""
+    g = len(problems)
+    arr = (Problem * max(g, 1))()
+    for i, pr in enumerate(problems):
+        m_, n_, k_ = (int(x) for x in pr[:3])
+        arr[i] = Problem(m_, n_, k_, int(pr[3]) if len(pr) > 3 else 0)
+    out = ctypes.c_void_p()
+    st = _lib.nvfp4_gg_plan_problems(ctypes.byref(out), g, arr if g else None, int(device), int(scale_layout))
+    if st != OK:
+        raise Nvfp4GGError(st, "nvfp4_gg_plan_problems")
+    plan = Plan(out.value, [int(pr[0]) for pr in problems], 0, 0)
+    plan.problems = [tuple(int(x) for x in pr) for pr in problems]
+    return plan
 
 
 def nvfp4_gg_blocked_scale_bytes(rows: int, k: int) -> int:

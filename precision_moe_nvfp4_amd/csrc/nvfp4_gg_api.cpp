@@ -29,7 +29,8 @@ using namespace nvfp4gg;
 
 struct nvfp4_gg_plan_s {
     uint32_t magic;
-    int g, n, k;
+    int g;
+    int n, k;                    // shared by every group, or 0 where the groups differ
     int device;
     int num_cus;
     int variant;
@@ -40,6 +41,7 @@ struct nvfp4_gg_plan_s {
     int grid;
     double est_cycles;           // estimated makespan of the tile schedule
     std::vector<int> m;          // caller order
+    std::vector<int> ns, ks, ldcs;  // caller order
     std::vector<int> order;      // order[p] = caller group at schedule position p
     std::vector<int> tile_begin; // per-group tile prefix in schedule order (informational)
     std::vector<TileDesc> tiles; // tiles grouped by workgroup (group = schedule position)
@@ -86,21 +88,23 @@ struct Schedule {
     std::vector<std::vector<TileDesc>> per_wg;
 };
 
-// Build and balance the tile list for chunk height R (group indices are schedule positions).
-Schedule build_schedule(int R, const std::vector<int>& m_sched, int n, int k, int num_wgs)
+// Build and balance the tile list for chunk height R (group indices are schedule positions;
+// group gi has m_sched[gi] rows, n_sched[gi] columns and K = k_sched[gi]).
+Schedule build_schedule(int R, const std::vector<int>& m_sched, const std::vector<int>& n_sched,
+                        const std::vector<int>& k_sched, int num_wgs)
 {
     Schedule S;
     S.chunk_rows = R;
     S.per_wg.assign(num_wgs, {});
-    const int ntiles_n = ceil_div(n, kTileCols);
     struct Cls {
         double cost;
         std::vector<std::pair<double, TileDesc>> tiles;
     };
     std::vector<Cls> classes;
     for (int gi = 0; gi < (int)m_sched.size(); ++gi) {
-        const int mi = m_sched[gi];
+        const int mi = m_sched[gi], k = k_sched[gi];
         if (mi <= 0) continue;
+        const int ntiles_n = ceil_div(n_sched[gi], kTileCols);
         const int chunks = ceil_div(mi, R);
         const int rp = (ceil_div(mi, chunks) + 31) / 32 * 32;
         for (int tn = 0; tn < ntiles_n; ++tn) {
@@ -187,11 +191,27 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_layout(nvfp4_gg_plan_t* out, int g, c
 {
     if (out == nullptr) return NVFP4_GG_EINVAL;
     *out = nullptr;
-    if (scale_layout != NVFP4_GG_SCALES_ROW_MAJOR && scale_layout != NVFP4_GG_SCALES_BLOCKED) return NVFP4_GG_EINVAL;
-    if (m == nullptr || g < 1 || n < 1 || k < 256 || (k % 256) != 0) return NVFP4_GG_EINVAL;
+    if (m == nullptr || g < 1) return NVFP4_GG_EINVAL;
     if (g > NVFP4_GG_MAX_GROUPS) return NVFP4_GG_EUNSUPPORTED;
-    for (int i = 0; i < g; ++i)
-        if (m[i] < 0 || m[i] > kMaxRows) return NVFP4_GG_EINVAL;
+    nvfp4_gg_problem_t probs[NVFP4_GG_MAX_GROUPS];
+    for (int i = 0; i < g; ++i) probs[i] = nvfp4_gg_problem_t{m[i], n, k, 0};
+    return nvfp4_gg_plan_problems(out, g, probs, device, scale_layout);
+}
+
+extern "C" nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g, const nvfp4_gg_problem_t* problems,
+                                                    int device, int scale_layout)
+{
+    if (out == nullptr) return NVFP4_GG_EINVAL;
+    *out = nullptr;
+    if (scale_layout != NVFP4_GG_SCALES_ROW_MAJOR && scale_layout != NVFP4_GG_SCALES_BLOCKED) return NVFP4_GG_EINVAL;
+    if (problems == nullptr || g < 1) return NVFP4_GG_EINVAL;
+    if (g > NVFP4_GG_MAX_GROUPS) return NVFP4_GG_EUNSUPPORTED;
+    for (int i = 0; i < g; ++i) {
+        const nvfp4_gg_problem_t& q = problems[i];
+        if (q.m < 0 || q.m > kMaxRows || q.n < 1 || q.n > kMaxRows || q.k < 256 || q.k > kMaxRows ||
+            (q.k % 256) != 0 || q.ldc < 0 || (q.ldc != 0 && q.ldc < q.n))
+            return NVFP4_GG_EINVAL;
+    }
     if (device < NVFP4_GG_DEVICE_NONE) return NVFP4_GG_EINVAL;
 
     int num_cus = kNominalCUs;
@@ -208,27 +228,45 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_layout(nvfp4_gg_plan_t* out, int g, c
     try {
         p->magic = kPlanMagic;
         p->g = g;
-        p->n = n;
-        p->k = k;
         p->device = device;
         p->num_cus = num_cus;
         p->scale_layout = scale_layout;
         p->variant = scale_layout == NVFP4_GG_SCALES_BLOCKED ? kVariantPersistentBlocked : kVariantPersistent;
         p->shape = variant_shape(p->variant);
-        p->m.assign(m, m + g);
+        p->m.resize(g);
+        p->ns.resize(g);
+        p->ks.resize(g);
+        p->ldcs.resize(g);
+        for (int i = 0; i < g; ++i) {
+            p->m[i] = problems[i].m;
+            p->ns[i] = problems[i].n;
+            p->ks[i] = problems[i].k;
+            p->ldcs[i] = problems[i].ldc ? problems[i].ldc : problems[i].n;
+        }
+        p->n = p->ns[0];
+        p->k = p->ks[0];
+        for (int i = 1; i < g; ++i) {
+            if (p->ns[i] != p->n) p->n = 0;
+            if (p->ks[i] != p->k) p->k = 0;
+        }
 
-        // schedule order of the groups: largest first (stable for ties)
+        // schedule order of the groups: largest work first (stable for ties)
+        const auto work = [&](int i) { return (double)p->m[i] * p->ns[i] * p->ks[i]; };
         p->order.resize(g);
         std::iota(p->order.begin(), p->order.end(), 0);
-        std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) { return m[a] > m[b]; });
-        std::vector<int> m_sched(g);
-        for (int s = 0; s < g; ++s) m_sched[s] = m[p->order[s]];
+        std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) { return work(a) > work(b); });
+        std::vector<int> m_sched(g), n_sched(g), k_sched(g);
+        for (int s = 0; s < g; ++s) {
+            m_sched[s] = p->m[p->order[s]];
+            n_sched[s] = p->ns[p->order[s]];
+            k_sched[s] = p->ks[p->order[s]];
+        }
 
         // pick the chunk height with the smallest estimated makespan
         Schedule best;
         bool have = false;
         for (int R : {96, 64, 32}) {
-            Schedule S = build_schedule(R, m_sched, n, k, num_cus);
+            Schedule S = build_schedule(R, m_sched, n_sched, k_sched, num_cus);
             if (!have || S.makespan < best.makespan * 0.999) {
                 best = std::move(S);
                 have = true;
@@ -259,10 +297,9 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_layout(nvfp4_gg_plan_t* out, int g, c
 
         // informational per-group tile prefix (schedule order)
         p->tile_begin.assign(g + 1, 0);
-        const int ntn = ceil_div(n, kTileCols);
         for (int s = 0; s < g; ++s) {
             const int chunks = m_sched[s] ? ceil_div(m_sched[s], p->chunk_rows) : 0;
-            p->tile_begin[s + 1] = p->tile_begin[s] + chunks * ntn;
+            p->tile_begin[s + 1] = p->tile_begin[s] + chunks * ceil_div(n_sched[s], kTileCols);
         }
     } catch (...) {
         delete p;
@@ -303,14 +340,15 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
     KernArgs args;
     std::memset(&args, 0, sizeof(args));
     args.g = plan->g;
-    args.n = plan->n;
-    args.k = plan->k;
     args.ntiles = plan->total_tiles;
     for (int s = 0; s < plan->g; ++s) {
         const int i = plan->order[s];
         const int mi = plan->m[i];
         GroupArgs& G = args.grp[s];
         G.m = mi;
+        G.n = plan->ns[i];
+        G.k = plan->ks[i];
+        G.ldc = plan->ldcs[i];
         if (mi > 0) {
             if (!A[i] || !B[i] || !SFA[i] || !SFB[i] || !C[i]) return NVFP4_GG_EINVAL;
             if (!aligned16(A[i]) || !aligned16(B[i]) || !aligned16(SFA[i]) || !aligned16(SFB[i]) || !aligned16(C[i]))

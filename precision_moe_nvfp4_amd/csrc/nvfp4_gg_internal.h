@@ -15,9 +15,11 @@ struct GroupArgs {
     const uint8_t* b;    // [n][k/2] packed E2M1
     const uint8_t* sfa;  // [m][k/16] E4M3FN
     const uint8_t* sfb;  // [n][k/16] E4M3FN
-    uint16_t* c;         // [m][n] fp16 bits
+    uint16_t* c;         // [m][ldc] fp16 bits (columns < n written)
     int m;               // rows of this group
-    int pad_;
+    int n;               // columns of C (rows of B)
+    int k;               // K (multiple of 256)
+    int ldc;             // C row stride in elements (>= n)
 };
 
 // One output tile: rows [row0, row0 + rows) of group `group` (schedule index), columns
@@ -33,8 +35,6 @@ struct TileDesc {
 // the tile list (built once by the planner) lives in device memory owned by the plan.
 struct KernArgs {
     int g;
-    int n;
-    int k;
     int ntiles;
     const TileDesc* tiles;  // tiles[b]: first tile of workgroup b (rows = 0: none)
     const int* wg_begin;    // workgroup b then processes tiles[wg_begin[b] .. wg_begin[b+1])

@@ -395,7 +395,7 @@ __device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2],
 // partner reads are in flight together.
 template <int NRB, int T>
 __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], uint8_t* smem,
-                                                  uint16_t* __restrict__ c0, int n, int rows, int col, int wave,
+                                                  uint16_t* __restrict__ c0, int n, int ldc, int rows, int col, int wave,
                                                   int lane)
 {
     using namespace pk;
@@ -427,7 +427,7 @@ __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], u
             }
     const int j = lane & 31, h = lane >> 5;
     // the whole tile is in bounds with 8-byte aligned rows: one uniform test
-    const bool full = (n & 3) == 0 && col + BN <= n;
+    const bool full = (ldc & 3) == 0 && col + BN <= n;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -444,7 +444,7 @@ __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], u
             if (r >= rows) continue;
             const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
             const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
-            uint16_t* crow = c0 + (long)r * n;
+            uint16_t* crow = c0 + (long)r * ldc;
             const int cc = col + 64 * cw + 32 * c + 8 * T + 4 * h;
             if (full) {
                 *reinterpret_cast<u2_t*>(crow + cc) =
@@ -460,13 +460,13 @@ __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], u
 
 template <int NRB>
 __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uint8_t* smem, uint16_t* __restrict__ c0,
-                                                int n, int rows, int col, int wave, int lane)
+                                                int n, int ldc, int rows, int col, int wave, int lane)
 {
     switch (wave >> 1) {   // the wave's K quarter (wave-uniform)
-    case 0: pk_reduce_store_q<NRB, 0>(acc, smem, c0, n, rows, col, wave, lane); break;
-    case 1: pk_reduce_store_q<NRB, 1>(acc, smem, c0, n, rows, col, wave, lane); break;
-    case 2: pk_reduce_store_q<NRB, 2>(acc, smem, c0, n, rows, col, wave, lane); break;
-    default: pk_reduce_store_q<NRB, 3>(acc, smem, c0, n, rows, col, wave, lane); break;
+    case 0: pk_reduce_store_q<NRB, 0>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
+    case 1: pk_reduce_store_q<NRB, 1>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
+    case 2: pk_reduce_store_q<NRB, 2>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
+    default: pk_reduce_store_q<NRB, 3>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
     }
 }
 
@@ -614,7 +614,8 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
 
     // all loads have landed (the last superstep was waited for) and no wave reads the ring
     // any more: the reduction area may overwrite it
-    pk_reduce_store<NRB>(acc, smem, G.c + (long)row0 * n, n, rows, col0, wave, lane);
+    const int ldc = __builtin_amdgcn_readfirstlane(G.ldc);
+    pk_reduce_store<NRB>(acc, smem, G.c + (long)row0 * ldc, n, ldc, rows, col0, wave, lane);
     // the next tile's loads reuse the LDS just read
     barrier_lds();
 }
@@ -639,7 +640,7 @@ __device__ __forceinline__ void pk_persistent(uint8_t* smem)
         const TileDesc t = {__builtin_amdgcn_readfirstlane(tv.group), __builtin_amdgcn_readfirstlane(tv.row0),
                             __builtin_amdgcn_readfirstlane(tv.rows), __builtin_amdgcn_readfirstlane(tv.col0)};
         const GroupArgs& G = args.grp[t.group];
-        const int n = args.n, k = args.k;
+        const int n = G.n, k = G.k;
         switch ((t.rows + 31) >> 5) {   // the planner keeps tiles within 0 .. RMAX rows
         case 1: pk_tile<1, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         case 2: pk_tile<2, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;

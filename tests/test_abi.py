@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {
-        "nvfp4_gg_plan", "nvfp4_gg_plan_layout", "nvfp4_gg_run", "nvfp4_gg_plan_info", "nvfp4_gg_destroy",
+        "nvfp4_gg_plan", "nvfp4_gg_plan_layout", "nvfp4_gg_plan_problems", "nvfp4_gg_run", "nvfp4_gg_plan_info", "nvfp4_gg_destroy",
         "nvfp4_gg_status_string", "nvfp4_gg_blocked_scale_bytes", "nvfp4_gg_scales_to_blocked"}
 
 
@@ -152,3 +152,31 @@ def test_scales_to_blocked_validates_before_touching_the_device():
     assert L.nvfp4_gg_scales_to_blocked(None, vp(32), 10, 256, None) == gg.EINVAL
     assert L.nvfp4_gg_scales_to_blocked(vp(16), vp(36), 10, 256, None) == gg.EALIGN
     assert L.nvfp4_gg_scales_to_blocked(None, None, 0, 256, None) == gg.OK
+
+
+@pytest.mark.parametrize("problems", [
+    [(4, 0, 256, 0)], [(4, 64, 128, 0)], [(4, 64, 300, 0)], [(-1, 64, 256, 0)], [(4, 64, 256, 63)],
+    [(4, 64, 256, -1)], [(4, (1 << 20) + 1, 256, 0)], [(1, 64, 256, 0), (1, 64, (1 << 20) + 256, 0)],
+])
+def test_plan_problems_rejects_bad_sizes(problems):
+    with pytest.raises(gg.Nvfp4GGError) as e:
+        gg.nvfp4_gg_plan_problems(problems, device=gg.DEVICE_NONE)
+    assert e.value.status == gg.EINVAL
+
+
+def test_plan_problems_mixed_sizes():
+    probs = [(100, 256, 512, 0), (0, 1000, 256, 0), (300, 130, 1024, 136), (7, 64, 256, 64)]
+    plan = gg.nvfp4_gg_plan_problems(probs, device=gg.DEVICE_NONE)
+    info = gg.nvfp4_gg_plan_info(plan)
+    assert info.g == 4 and info.n == 0 and info.k == 0        # sizes differ between groups
+    # largest work first: m * n * k
+    work = [m * n * k for m, n, k, _ in probs]
+    order = [info.order[s] for s in range(4)]
+    assert order == sorted(range(4), key=lambda i: -work[i])
+    tiles = [(probs[i][0] + info.tile_m - 1) // info.tile_m * ((probs[i][1] + 127) // 128) if probs[i][0] else 0
+             for i in order]
+    assert [info.tile_begin[s + 1] - info.tile_begin[s] for s in range(4)] == tiles
+    # uniform sizes report n and k
+    plan2 = gg.nvfp4_gg_plan_problems([(10, 256, 512), (20, 256, 512)], device=gg.DEVICE_NONE)
+    info2 = gg.nvfp4_gg_plan_info(plan2)
+    assert (info2.n, info2.k) == (256, 512)
