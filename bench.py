@@ -41,6 +41,9 @@ KERNEL_SOURCE = os.path.join(ROOT, "precision_moe_nvfp4_amd", "csrc", "nvfp4_gg_
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_gg_c1.md")
 
 
+DENSE = "8192:4096:4096"
+
+
 def algorithmic_bytes(m, n, k):
     """Each operand byte read once, C written once: A + B + SFA + SFB + C(fp16)."""
     sm, g = sum(m), len(m)
@@ -228,7 +231,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--shapes", default="c1,c2,c3,c4")
+    # c1..c4: the grouped workloads; DENSE: one large group (g = 1, m = 8192, n = k = 4096)
+    ap.add_argument("--shapes", default="c1,c2,c3,c4," + DENSE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--cold-only", action="store_true",

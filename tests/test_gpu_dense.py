@@ -1,0 +1,46 @@
+"""Dense single-group workload (g = 1, large m): the whole GEMM runs on the GPU at full size in
+the launch configuration the bench times; the oracle recomputes a sample of rows (one full
+96-row tile and its neighbours, the last rows, and random rows), which are compared element by
+element with the usual bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_moe_nvfp4_amd as gg
+from synthetic import make_inputs
+from test_gpu_parity import CANARY, PAD, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("m,n,k", [(8192, 4096, 4096), (3000, 1000, 2048)])
+def test_dense_single_group_sampled_rows(m, n, k):
+    say(f"dense m={m} n={n} k={k}")
+    inp = make_inputs([m], n, k, seed=4242)
+    dev = torch.device("cuda", 0)
+    A, B, SFA, SFB = gg.device_operands(inp.A, inp.B, inp.SFA, inp.SFB, dev)
+    buf = torch.full((PAD + m * n + PAD,), CANARY, dtype=torch.int16, device=dev)
+    plan = gg.nvfp4_gg_plan([m], n, k)
+    gg.nvfp4_gg_run(plan, A, B, SFA, SFB, [buf[PAD:PAD + m * n]])
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy().view(np.uint16)
+    assert np.all(h[:PAD] == CANARY) and np.all(h[PAD + m * n:] == CANARY)
+    C = h[PAD:PAD + m * n].reshape(m, n)
+    assert not np.any(C == CANARY), "unwritten elements"
+    rng = np.random.default_rng(m + n + k)
+    rows = sorted(set(range(96, 192)) | {0, 1, 95, 192, m - 2, m - 1} |
+                  set(int(x) for x in rng.integers(0, m, 40)))
+    rows = np.array([r for r in rows if r < m])
+    ref = oracle.grouped([len(rows)], n, k, [np.ascontiguousarray(inp.A[0][rows])], [inp.B[0]],
+                         [np.ascontiguousarray(inp.SFA[0][rows])], [inp.SFB[0]], want_abs=True)
+    got = C[rows]
+    r16 = ref.C[0]
+    gv = got.view(np.float16).astype(np.float64)
+    rv = r16.view(np.float16).astype(np.float64)
+    tol = oracle.tolerance(r16, ref.abssum[0])
+    bad = np.abs(gv - rv) > tol
+    mism = int(np.sum((got != r16) & ((got | r16) & 0x7FFF != 0)))
+    say(f"dense: {got.size} sampled elements, {int(bad.sum())} beyond tolerance, {mism} fp16 bit mismatches")
+    assert not bad.any()
