@@ -92,7 +92,7 @@ typedef enum {
  * addresses C through per-group strides.
  *   m   rows of A_i and C_i (0 <= m <= 2^20; 0: nothing is read or written for the group)
  *   n   rows of B_i and columns of C_i (1 <= n <= 2^20)
- *   k   K of the group (256 <= k <= 2^20, k % 256 == 0)
+ *   k   K of the group (64 <= k <= 2^20, k % 64 == 0)
  *   ldc elements between the starts of consecutive rows of C_i: 0 means n, otherwise >= n;
  *       the elements of a row beyond column n are never written
  */
@@ -126,10 +126,11 @@ typedef struct {
  * NVFP4_GG_ENOMEM).  Plans are meant to be built once per shape and reused.
  *   device: HIP device ordinal, -1 for the current device, or NVFP4_GG_DEVICE_NONE (host
  *   only: nothing is allocated on a device).
- * Requirements: 1 <= g <= NVFP4_GG_MAX_GROUPS, n >= 1, k >= 256 and k % 256 == 0 (the
- * K granularity the group_gemm host function of "kernelindex submission 498317"
- * requires), 0 <= m_i <= 2^20; else NVFP4_GG_EINVAL (g above the maximum:
- * NVFP4_GG_EUNSUPPORTED).  A device that is not gfx950: NVFP4_GG_EUNSUPPORTED.
+ * Requirements: 1 <= g <= NVFP4_GG_MAX_GROUPS, 1 <= n <= 2^20, 64 <= k <= 2^20 and
+ * k % 64 == 0, 0 <= m_i <= 2^20; else NVFP4_GG_EINVAL (g above the maximum:
+ * NVFP4_GG_EUNSUPPORTED).  (The group_gemm host function of "kernelindex submission
+ * 498317" requires k % 256 == 0; here K values beyond the last multiple of 256 are handled
+ * by a shorter last K step, so every multiple of 64 is accepted.)  A device that is not gfx950: NVFP4_GG_EUNSUPPORTED.
  * On success *out holds a new plan, released with nvfp4_gg_destroy; on failure *out = NULL.
  */
 nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
@@ -158,7 +159,7 @@ nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g, const nvfp
                                          int device, int scale_layout);
 
 /* Bytes of a NVFP4_GG_SCALES_BLOCKED scale tensor with `rows` rows (0 if rows <= 0 or
- * k is not a positive multiple of 256). */
+ * k is not a positive multiple of 64). */
 size_t nvfp4_gg_blocked_scale_bytes(int rows, int k);
 
 /*
@@ -167,8 +168,8 @@ size_t nvfp4_gg_blocked_scale_bytes(int rows, int k);
  * (nvfp4_gg_blocked_scale_bytes(rows, k) bytes, every one written; padding rows are
  * written as zero).  Both are device pointers of the current device, 16-byte aligned
  * (else NVFP4_GG_EALIGN), non-null for rows > 0, not overlapping (else undefined).
- * rows = 0 does nothing.  Requirements: 0 <= rows <= 2^20, k >= 256, k % 256 == 0, else
- * NVFP4_GG_EINVAL.  A failed launch returns NVFP4_GG_EHIP.  Asynchronous, like
+ * rows = 0 does nothing.  Requirements: 0 <= rows <= 2^20, 64 <= k <= 2^20, k % 64 == 0,
+ * else NVFP4_GG_EINVAL.  A failed launch returns NVFP4_GG_EHIP.  Asynchronous, like
  * nvfp4_gg_run; it allocates nothing.
  */
 nvfp4_gg_status_t nvfp4_gg_scales_to_blocked(void* dst, const void* src, int rows, int k,

@@ -75,7 +75,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 double tile_cycles(int rows, int k)
 {
     const int rpad = (rows + 31) & ~31;
-    const int steps = k / kStepK;
+    const int steps = (k + 255) / 256 * (256 / kStepK);   // a short last superstep costs a full one
     const double mfma = 4.0 * (rpad / 32) * 35.0;
     const double valu = (2.0 * 26.0 + 18.0 * ((rpad + 63) / 64)) * 4.6;
     const double load = (kTileCols + rpad) * 36.0 / 21.0;
@@ -208,8 +208,8 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g,
     if (g > NVFP4_GG_MAX_GROUPS) return NVFP4_GG_EUNSUPPORTED;
     for (int i = 0; i < g; ++i) {
         const nvfp4_gg_problem_t& q = problems[i];
-        if (q.m < 0 || q.m > kMaxRows || q.n < 1 || q.n > kMaxRows || q.k < 256 || q.k > kMaxRows ||
-            (q.k % 256) != 0 || q.ldc < 0 || (q.ldc != 0 && q.ldc < q.n))
+        if (q.m < 0 || q.m > kMaxRows || q.n < 1 || q.n > kMaxRows || q.k < 64 || q.k > kMaxRows ||
+            (q.k % 64) != 0 || q.ldc < 0 || (q.ldc != 0 && q.ldc < q.n))
             return NVFP4_GG_EINVAL;
     }
     if (device < NVFP4_GG_DEVICE_NONE) return NVFP4_GG_EINVAL;
@@ -231,7 +231,11 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g,
         p->device = device;
         p->num_cus = num_cus;
         p->scale_layout = scale_layout;
-        p->variant = scale_layout == NVFP4_GG_SCALES_BLOCKED ? kVariantPersistentBlocked : kVariantPersistent;
+        bool all256 = true;
+        for (int i = 0; i < g; ++i) all256 = all256 && (problems[i].k % 256) == 0;
+        p->variant = scale_layout == NVFP4_GG_SCALES_BLOCKED ? kVariantPersistentBlocked
+                     : all256                                ? kVariantPersistent
+                                                             : kVariantPersistentKTail;
         p->shape = variant_shape(p->variant);
         p->m.resize(g);
         p->ns.resize(g);
@@ -397,14 +401,14 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_p
 
 extern "C" size_t nvfp4_gg_blocked_scale_bytes(int rows, int k)
 {
-    if (rows <= 0 || k < 256 || (k % 256) != 0) return 0;
+    if (rows <= 0 || k < 64 || (k % 64) != 0) return 0;
     return (size_t)blocked_scale_bytes(rows, k);
 }
 
 extern "C" nvfp4_gg_status_t nvfp4_gg_scales_to_blocked(void* dst, const void* src, int rows, int k,
                                                         hipStream_t stream)
 {
-    if (rows < 0 || rows > kMaxRows || k < 256 || (k % 256) != 0) return NVFP4_GG_EINVAL;
+    if (rows < 0 || rows > kMaxRows || k < 64 || k > kMaxRows || (k % 64) != 0) return NVFP4_GG_EINVAL;
     if (rows == 0) return NVFP4_GG_OK;
     if (dst == nullptr || src == nullptr) return NVFP4_GG_EINVAL;
     if (!aligned16(dst) || !aligned16(src)) return NVFP4_GG_EALIGN;

@@ -18,7 +18,7 @@ struct GroupArgs {
     uint16_t* c;         // [m][ldc] fp16 bits (columns < n written)
     int m;               // rows of this group
     int n;               // columns of C (rows of B)
-    int k;               // K (multiple of 256)
+    int k;               // K (multiple of 64)
     int ldc;             // C row stride in elements (>= n)
 };
 
@@ -50,6 +50,7 @@ struct VariantShape {
 enum Variant : int {
     kVariantPersistent = 2,         // persistent 8-wave workgroups over a planned tile list
     kVariantPersistentBlocked = 3,  // the same, reading 128x4 blocked scale tensors
+    kVariantPersistentKTail = 4,    // row-major scales when some k is not a multiple of 256
 };
 
 VariantShape variant_shape(int variant);
@@ -57,7 +58,8 @@ VariantShape variant_shape(int variant);
 // Enqueue one launch of `variant` with `grid` workgroups.
 hipError_t launch_variant(int variant, const KernArgs& args, int grid, hipStream_t stream);
 
-// Bytes of a 128x4 blocked scale tensor: ceil(rows / 128) row blocks of k / 64 atoms of 512 B.
+// Bytes of a 128x4 blocked scale tensor: ceil(rows / 128) row blocks of k / 64 atoms of 512 B
+// (k a multiple of 64).
 inline long blocked_scale_bytes(int rows, int k)
 {
     return rows <= 0 ? 0 : (long)((rows + 127) / 128) * (k / 64) * 512;

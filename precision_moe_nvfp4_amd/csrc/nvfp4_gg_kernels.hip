@@ -133,13 +133,24 @@ static_assert(8 * RED_WAVE <= LDS_BYTES, "reduction area must fit in LDS");
 // Loads
 // ---------------------------------------------------------------------------------------
 
+// How the scales are fetched (see SuperLoads).
+enum ScaleMode : int {
+    SCL_ROW16 = 0,    // row-major scales, 16 bytes per lane (k % 256 == 0: 16-byte rows)
+    SCL_BLOCKED = 1,  // 128x4 blocked scales, 4 bytes per lane
+    SCL_ROW4 = 2,     // row-major scales, 4 bytes per lane (rows only 4-byte aligned)
+};
+
 // Per-wave direct-to-LDS loads of one superstep.  B code instruction i (rows 8i .. +8,
 // i < 16) goes to wave i % 8 and A code instruction a (rows 8a .. +8) to wave (a + 4) % 8.
-// Scales, row-major layout: B scale instruction q (rows 32q .. +32, 16 bytes per lane,
-// lanes < 32) to wave q < 4, A scale instruction q to wave 7 - q.  Scales, 128x4 blocked
-// layout: 4 bytes per lane, so instruction q covers rows 16q .. +16; B scale instruction q
-// to wave q (all 8), A scale instruction q to wave q.  Either way the LDS copy of a
-// superstep's scales is the same: row r's 16 bytes at 16 r.
+// Scales, SCL_ROW16: B scale instruction q (rows 32q .. +32, 16 bytes per lane, lanes < 32)
+// to wave q < 4, A scale instruction q to wave 7 - q.  Scales, SCL_BLOCKED and SCL_ROW4:
+// 4 bytes per lane, so instruction q covers rows 16q .. +16 (lane l: row 16q + l / 4,
+// scale dword l % 4 of the superstep); B scale instruction q to wave q (all 8), A scale
+// instruction q to wave q.  Either way the LDS copy of a superstep's scales is the same:
+// row r's 16 bytes at 16 r.  In a last superstep that holds fewer than 256 K values, lanes
+// whose code chunk or scale dword lies beyond K store zeros to their LDS place instead of
+// loading (zero codes and zero scales contribute exact zeros); every instruction keeps at
+// least one loading lane, so the per-superstep load count is unchanged.
 struct SuperLoads {
     const uint8_t* b[2];  // B codes of this lane, superstep 0
     const uint8_t* sb;    // B scales of this lane
@@ -153,10 +164,14 @@ struct SuperLoads {
     int na;               // A code instructions of this wave (0 .. 2)
     int nsa;              // A scale instructions of this wave (0 or 1)
     int ops;              // loads per superstep issued by this wave
+    int b_chunk[2];       // global 16-byte chunk (0 .. 7) of a row that this lane loads
+    int a_chunk[2];
+    int s_dword;          // scale dword (0 .. 3) of the superstep this lane loads (4-byte modes)
+    long sstride;         // scale bytes between consecutive supersteps of this lane
 };
 
 // Loads per superstep issued by wave w for tiles of 32 nrb rows (the assignment above).
-__host__ __device__ constexpr int pk_ops(int w, int nrb, bool blocked)
+__host__ __device__ constexpr int pk_ops(int w, int nrb, bool blocked)   // blocked: 4-byte scale loads
 {
     int ops = 2;                                            // B codes: instructions w, w + 8
     ops += blocked ? 1 : (w < 4 ? 1 : 0);                   // B scales
@@ -177,25 +192,54 @@ __host__ __device__ constexpr int pk_ops_max(int nrb, bool blocked)
     return v;
 }
 
-template <bool BLK>
-__device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, const SuperLoads& L, int lane)
+// 16 code bytes of this lane, or zeros when its chunk lies beyond the superstep's K.
+__device__ __forceinline__ void pk_load16(const uint8_t* src, uint8_t* lds_base, int lane, bool valid)
+{
+    if (valid) {
+        __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+    } else {
+        *reinterpret_cast<u4_t*>(lds_base + 16 * lane) = u4_t{0u, 0u, 0u, 0u};
+    }
+}
+
+// Issue the loads of superstep t (kt = K values it holds, 256 except maybe in the last).
+template <int SCL>
+__device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, int kt, const SuperLoads& L, int lane)
 {
     using namespace pk;
     const long kb = (long)t * ROWB;
-    __builtin_amdgcn_global_load_lds(L.b[0] + kb, slot_base + L.b_dst[0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(L.b[1] + kb, slot_base + L.b_dst[1], 16, 0, 0);
-    if constexpr (BLK) {
-        // four 512-byte atoms (4 scales x 128 rows each) per superstep
-        const long ks = (long)t * (4 * 512);
-        if (L.nsb > 0) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 4, 0, 0);
-        if (L.nsa > 0) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 4, 0, 0);
+    const long ks = (long)t * L.sstride;
+    if (SCL == SCL_ROW16 || kt == SK) {   // (SCL_ROW16 plans have no short supersteps)
+        __builtin_amdgcn_global_load_lds(L.b[0] + kb, slot_base + L.b_dst[0], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(L.b[1] + kb, slot_base + L.b_dst[1], 16, 0, 0);
+        if constexpr (SCL == SCL_ROW16) {
+            if (L.nsb > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 16, 0, 0);
+            if (L.nsa > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 16, 0, 0);
+        } else {
+            if (L.nsb > 0) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 4, 0, 0);
+            if (L.nsa > 0) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 4, 0, 0);
+        }
+        if (L.na > 0) __builtin_amdgcn_global_load_lds(L.a[0] + kb, slot_base + L.a_dst[0], 16, 0, 0);
+        if (L.na > 1) __builtin_amdgcn_global_load_lds(L.a[1] + kb, slot_base + L.a_dst[1], 16, 0, 0);
     } else {
-        const long ks = (long)t * SCB;
-        if (L.nsb > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 16, 0, 0);
-        if (L.nsa > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 16, 0, 0);
+        // a short last superstep: kt / 32 code chunks and kt / 64 scale dwords per row
+        const int vchunks = kt >> 5, vdw = kt >> 6;
+        pk_load16(L.b[0] + kb, slot_base + L.b_dst[0], lane, L.b_chunk[0] < vchunks);
+        pk_load16(L.b[1] + kb, slot_base + L.b_dst[1], lane, L.b_chunk[1] < vchunks);
+        if constexpr (SCL != SCL_ROW16) {
+            const bool sv = L.s_dword < vdw;
+            if (L.nsb > 0) {
+                if (sv) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 4, 0, 0);
+                else *reinterpret_cast<uint32_t*>(slot_base + L.sb_dst + 4 * lane) = 0u;
+            }
+            if (L.nsa > 0) {
+                if (sv) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 4, 0, 0);
+                else *reinterpret_cast<uint32_t*>(slot_base + L.sa_dst + 4 * lane) = 0u;
+            }
+        }
+        if (L.na > 0) pk_load16(L.a[0] + kb, slot_base + L.a_dst[0], lane, L.a_chunk[0] < vchunks);
+        if (L.na > 1) pk_load16(L.a[1] + kb, slot_base + L.a_dst[1], lane, L.a_chunk[1] < vchunks);
     }
-    if (L.na > 0) __builtin_amdgcn_global_load_lds(L.a[0] + kb, slot_base + L.a_dst[0], 16, 0, 0);
-    if (L.na > 1) __builtin_amdgcn_global_load_lds(L.a[1] + kb, slot_base + L.a_dst[1], 16, 0, 0);
 }
 
 // Wait until at most n of this wave's loads are in flight (0 <= n <= 30).
@@ -220,11 +264,12 @@ __device__ __forceinline__ void pk_wait_loads(int n)
 // The same wait for the steady state of the ring, where a wave's count is one of two values
 // for a given tile height and scale layout (its share of the loads times the supersteps
 // left in flight): one uniform branch instead of a search over every count.
-template <int NRB, bool BLK>
+template <int NRB, int SCL>
 __device__ __forceinline__ void pk_wait_steady(int n)
 {
+    constexpr bool B4 = SCL != SCL_ROW16;
     constexpr int AHEAD = pk::ring_slots(32 * NRB) - 2;
-    constexpr int LO = AHEAD * pk_ops_min(NRB, BLK), HI = AHEAD * pk_ops_max(NRB, BLK);
+    constexpr int LO = AHEAD * pk_ops_min(NRB, B4), HI = AHEAD * pk_ops_max(NRB, B4);
     static_assert(HI <= 15, "the constant waits use the 4 low vmcnt bits");
     if (n == HI) {
         __builtin_amdgcn_s_waitcnt(0x0f70 | HI);   // vmcnt(HI); expcnt and lgkmcnt not waited for
@@ -476,8 +521,9 @@ __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uin
 
 // One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)).  All
 // 8 waves execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs
-// per B fragment; BLK selects the 128x4 blocked scale layout (else row-major scales).
-template <int NRB, bool BLK>
+// per B fragment; SCL is how the scales are fetched (ScaleMode).  K is a multiple of 64;
+// the last superstep holds k - 256 (supers - 1) K values.
+template <int NRB, int SCL>
 __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_, uint8_t* smem)
 {
     using namespace pk;
@@ -490,7 +536,8 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     const int cw = wave & 1, tq = wave >> 1;   // column half, K quarter
     const int j = lane & 31, h = lane >> 5;
     const int rpad = 32 * NRB;
-    const int supers = k / SK;
+    const int supers = (k + SK - 1) / SK;
+    const int klast = k - SK * (supers - 1);   // K values of the last superstep
     const long qs = k / 2, ss = k / 16;
 
     const int sbytes = slot_bytes(rpad), nslots = ring_slots(rpad);
@@ -509,6 +556,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             const int r = 8 * i + rl;
             L.b[q] = G.b + (long)min(col0 + r, n - 1) * qs + 16 * (pos ^ swz(r));
             L.b_dst[q] = 8 * i * ROWB;
+            L.b_chunk[q] = pos ^ swz(r);
         }
         const int na_total = rpad / 8;
         L.na = 0;
@@ -518,9 +566,11 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             const int r = 8 * a + rl;
             L.a[q] = G.a + (long)(row0 + min(r, rows - 1)) * qs + 16 * (pos ^ swz(r));
             L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
+            L.a_chunk[q] = pos ^ swz(r);
             if (a < na_total) L.na = q + 1;
         }
-        if constexpr (BLK) {
+        L.s_dword = lane & 3;
+        if constexpr (SCL == SCL_BLOCKED) {
             // 128x4 blocked scales: the scale of (row r, K block c) sits in 512-byte atom
             // (r / 128) * (k / 64) + c / 4 at byte 16 (r % 32) + 4 ((r / 32) % 4) + c % 4, so
             // the 4 scales of a row in one atom are contiguous.  Lane l of scale instruction
@@ -536,7 +586,21 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             L.nsa = wave < rpad / 16 ? 1 : 0;
             L.sa = G.sfa + ((long)(ga >> 7) * atoms + piece) * 512 + 16 * (ga & 31) + 4 * ((ga >> 5) & 3);
             L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
+            L.sstride = 4 * 512;             // four atoms per superstep
+        } else if constexpr (SCL == SCL_ROW4) {
+            // row-major scales, lane l of scale instruction q = wave: dword l % 4 of the
+            // superstep's 16 scale bytes of row 16 q + l / 4
+            const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
+            L.nsb = 1;
+            L.sb = G.sfb + (long)gb * ss + 4 * (lane & 3);
+            L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
+            const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
+            L.nsa = wave < rpad / 16 ? 1 : 0;
+            L.sa = G.sfa + (long)ga * ss + 4 * (lane & 3);
+            L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
+            L.sstride = SCB;
         } else {
+            L.sstride = SCB;
             L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
             L.sb = G.sfb + (long)min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) * ss;
             L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
@@ -559,9 +623,10 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     // 1 .. nslots-1; dequantise the A of superstep 0's first half and read the raw B
     // operand of its first step
     const int first = min(nslots, supers);
-    pk_issue<BLK>(ring, 0, L, lane);
+    const auto kt_of = [&](int t) { return t == supers - 1 ? klast : SK; };
+    pk_issue<SCL>(ring, 0, kt_of(0), L, lane);
     pk_wait_loads(0);
-    for (int t = 1; t < first; ++t) pk_issue<BLK>(ring + t * sbytes, t, L, lane);
+    for (int t = 1; t < first; ++t) pk_issue<SCL>(ring + t * sbytes, t, kt_of(t), L, lane);
     barrier_lds();
     uint8_t* a16h[2] = {a16, a16 + rpad * A_ROW};
     const int aoff = j * A_ROW + 128 * h + 32 * tq;   // this lane's A fragment row
@@ -591,7 +656,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // superstep t - 1 + nslots
         if (t > 0 && t - 1 + nslots < supers) {
             const int fs = (cs == 0) ? nslots - 1 : cs - 1;
-            pk_issue<BLK>(ring + fs * sbytes, t - 1 + nslots, L, lane);
+            pk_issue<SCL>(ring + fs * sbytes, t - 1 + nslots, kt_of(t - 1 + nslots), L, lane);
         }
         const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
         const uint8_t* cur = ring + cs * sbytes;
@@ -602,7 +667,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // superstep t + 1 must have landed before half 1 reads its bytes (loads complete in
         // issue order, so later supersteps may stay in flight)
         if (t + nslots - 1 < supers) {
-            pk_wait_steady<NRB, BLK>(wait_steady);   // supersteps t + 2 .. t + nslots - 1 in flight
+            pk_wait_steady<NRB, SCL>(wait_steady);   // supersteps t + 2 .. t + nslots - 1 in flight
         } else if (t + 1 < supers) {
             pk_wait_loads((supers - 2 - t) * L.ops);
         }
@@ -622,7 +687,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
 
 // Persistent kernel body: workgroup b processes its first tile tiles[b], then tiles
 // list[begin[b] .. begin[b+1]) in order.
-template <bool BLK>
+template <int SCL>
 __device__ __forceinline__ void pk_persistent(uint8_t* smem)
 {
     // index the group table in place in the kernarg segment (scalar loads), rather than
@@ -642,9 +707,9 @@ __device__ __forceinline__ void pk_persistent(uint8_t* smem)
         const GroupArgs& G = args.grp[t.group];
         const int n = G.n, k = G.k;
         switch ((t.rows + 31) >> 5) {   // the planner keeps tiles within 0 .. RMAX rows
-        case 1: pk_tile<1, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 2: pk_tile<2, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 3: pk_tile<3, BLK>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+        case 1: pk_tile<1, SCL>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+        case 2: pk_tile<2, SCL>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+        case 3: pk_tile<3, SCL>(G, n, k, t.row0, t.rows, t.col0, smem); break;
         default: break;
         }
         if (next >= i_end) break;
@@ -652,20 +717,28 @@ __device__ __forceinline__ void pk_persistent(uint8_t* smem)
     }
 }
 
-// Row-major scales ([rows][k/16]).
+// Row-major scales ([rows][k/16]), every k a multiple of 256.
 __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args_byval)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
     (void)args_byval;
-    pk_persistent<false>(smem);
+    pk_persistent<SCL_ROW16>(smem);
 }
 
-// 128x4 blocked scales (512-byte atoms).
+// 128x4 blocked scales (512-byte atoms), k a multiple of 64.
 __global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent_blocked(KernArgs args_byval)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
     (void)args_byval;
-    pk_persistent<true>(smem);
+    pk_persistent<SCL_BLOCKED>(smem);
+}
+
+// Row-major scales with some k not a multiple of 256 (scale rows only 4-byte aligned).
+__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent_ktail(KernArgs args_byval)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
+    (void)args_byval;
+    pk_persistent<SCL_ROW4>(smem);
 }
 
 VariantShape variant_shape(int variant)
@@ -673,6 +746,7 @@ VariantShape variant_shape(int variant)
     switch (variant) {
     case kVariantPersistent:
     case kVariantPersistentBlocked:
+    case kVariantPersistentKTail:
         return VariantShape{pk::RMAX, pk::BN, pk::THREADS, pk::LDS_BYTES};
     default:
         return VariantShape{0, 0, 0, 0};
@@ -690,6 +764,9 @@ hipError_t launch_variant(int variant, const KernArgs& args, int grid, hipStream
                                params, 0, stream);
     case kVariantPersistentBlocked:
         return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent_blocked), dim3(grid),
+                               dim3(pk::THREADS), params, 0, stream);
+    case kVariantPersistentKTail:
+        return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent_ktail), dim3(grid),
                                dim3(pk::THREADS), params, 0, stream);
     default:
         return hipErrorInvalidValue;

@@ -47,7 +47,7 @@ def raw_plan(g, m, n, k, device=gg.DEVICE_NONE):
 
 
 @pytest.mark.parametrize("g,m,n,k", [
-    (0, [], 64, 256), (1, [4], 0, 256), (1, [4], 64, 128), (1, [4], 64, 300), (1, [4], 64, 0),
+    (0, [], 64, 256), (1, [4], 0, 256), (1, [4], 64, 96), (1, [4], 64, 300), (1, [4], 64, 0), (1, [4], 64, 32),
     (1, [-1], 64, 256), (1, None, 64, 256), (2, [1, (1 << 20) + 1], 64, 256),
 ])
 def test_plan_rejects_bad_arguments(g, m, n, k):
@@ -138,7 +138,7 @@ def test_plan_layout_validation_and_info():
 
 @pytest.mark.parametrize("rows,k,expect", [
     (1, 256, 2048), (128, 256, 2048), (129, 256, 4096), (300, 1536, 3 * 24 * 512), (0, 256, 0), (-1, 256, 0),
-    (10, 128, 0), (10, 300, 0),
+    (10, 128, 1024), (200, 192, 2 * 3 * 512), (10, 96, 0), (10, 300, 0), (10, 32, 0),
 ])
 def test_blocked_scale_bytes(rows, k, expect):
     assert gg.nvfp4_gg_blocked_scale_bytes(rows, k) == expect
@@ -155,7 +155,7 @@ def test_scales_to_blocked_validates_before_touching_the_device():
 
 
 @pytest.mark.parametrize("problems", [
-    [(4, 0, 256, 0)], [(4, 64, 128, 0)], [(4, 64, 300, 0)], [(-1, 64, 256, 0)], [(4, 64, 256, 63)],
+    [(4, 0, 256, 0)], [(4, 64, 96, 0)], [(4, 64, 300, 0)], [(4, 64, 32, 0)], [(-1, 64, 256, 0)], [(4, 64, 256, 63)],
     [(4, 64, 256, -1)], [(4, (1 << 20) + 1, 256, 0)], [(1, 64, 256, 0), (1, 64, (1 << 20) + 256, 0)],
 ])
 def test_plan_problems_rejects_bad_sizes(problems):
@@ -180,3 +180,14 @@ def test_plan_problems_mixed_sizes():
     plan2 = gg.nvfp4_gg_plan_problems([(10, 256, 512), (20, 256, 512)], device=gg.DEVICE_NONE)
     info2 = gg.nvfp4_gg_plan_info(plan2)
     assert (info2.n, info2.k) == (256, 512)
+
+
+@pytest.mark.parametrize("k,variant", [(256, 2), (64, 4), (192, 4), (1088, 4), (7168, 2)])
+def test_k_granularity_and_variant(k, variant):
+    plan = gg.nvfp4_gg_plan([100, 7], 96, k, device=gg.DEVICE_NONE)
+    assert gg.nvfp4_gg_plan_info(plan).variant == variant
+    blocked = gg.nvfp4_gg_plan([100, 7], 96, k, device=gg.DEVICE_NONE, scale_layout=gg.SCALES_BLOCKED)
+    assert gg.nvfp4_gg_plan_info(blocked).variant == 3
+    # one group with a K tail moves the whole plan to the 4-byte scale variant
+    mixed = gg.nvfp4_gg_plan_problems([(10, 64, 512), (10, 64, k)], device=gg.DEVICE_NONE)
+    assert gg.nvfp4_gg_plan_info(mixed).variant == (2 if k % 256 == 0 else 4)

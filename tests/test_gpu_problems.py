@@ -54,3 +54,19 @@ def run_problems(problems, layout):
 def test_per_group_sizes_and_strides(case, layout):
     say(f"problems {CASES[case]} layout {layout}")
     run_problems(CASES[case], layout)
+
+
+# K not a multiple of 256: the last K step is short (64, 128 or 192 K values)
+KTAIL_CASES = [
+    [(17, 200, 64, 0)],
+    [(100, 130, 192, 0), (64, 130, 320, 136)],
+    [(300, 256, 1088, 0), (5, 256, 448, 0), (96, 256, 512, 0)],
+    [(129, 1000, 704, 1001), (0, 64, 128, 0), (64, 128, 2112, 0)],
+]
+
+
+@pytest.mark.parametrize("layout", [gg.SCALES_ROW_MAJOR, gg.SCALES_BLOCKED])
+@pytest.mark.parametrize("case", range(len(KTAIL_CASES)))
+def test_k_tails(case, layout):
+    say(f"k tails {KTAIL_CASES[case]} layout {layout}")
+    run_problems(KTAIL_CASES[case], layout)
