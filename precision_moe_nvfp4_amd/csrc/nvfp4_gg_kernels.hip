@@ -151,11 +151,19 @@ enum ScaleMode : int {
 // whose code chunk or scale dword lies beyond K store zeros to their LDS place instead of
 // loading (zero codes and zero scales contribute exact zeros); every instruction keeps at
 // least one loading lane, so the per-superstep load count is unchanged.
+// Source addresses are a workgroup-uniform base (first row of the tile, superstep 0) plus a
+// 32-bit per-lane offset, so that the loads address memory as scalar base + vector offset
+// and the per-superstep advance is a scalar add.
 struct SuperLoads {
-    const uint8_t* b[2];  // B codes of this lane, superstep 0
-    const uint8_t* sb;    // B scales of this lane
-    const uint8_t* a[2];  // A codes of this lane
-    const uint8_t* sa;    // A scales of this lane
+    const uint8_t* bb;    // B codes: uniform base
+    const uint8_t* sbb;   // B scales: uniform base
+    const uint8_t* ab;    // A codes: uniform base
+    const uint8_t* sab;   // A scales: uniform base
+    __amdgpu_buffer_rsrc_t rb, rsb, ra, rsa;   // buffer resources of the four bases
+    uint32_t b[2];        // this lane's offsets from the bases
+    uint32_t sb;
+    uint32_t a[2];
+    uint32_t sa;
     int b_dst[2];         // LDS offsets (inside a slot) of the B code instructions
     int sb_dst;
     int a_dst[2];
@@ -192,11 +200,33 @@ __host__ __device__ constexpr int pk_ops_max(int nrb, bool blocked)
     return v;
 }
 
+// Raw buffer resource over [base, base + 2^31): loads address it as scalar base + 32-bit
+// vector offset + scalar offset, so the per-lane part needs no 64-bit address arithmetic
+// and the per-superstep advance rides in the scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pk_rsrc(const uint8_t* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// Direct-to-LDS buffer loads of 16 / 4 bytes per lane at voff + soff into lds_base + 16 (4)
+// times the lane index.
+__device__ __forceinline__ void pk_bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, soff,
+                                             0, 0);
+}
+__device__ __forceinline__ void pk_bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voff, soff,
+                                             0, 0);
+}
+
 // 16 code bytes of this lane, or zeros when its chunk lies beyond the superstep's K.
-__device__ __forceinline__ void pk_load16(const uint8_t* src, uint8_t* lds_base, int lane, bool valid)
+__device__ __forceinline__ void pk_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds_base,
+                                          int lane, bool valid)
 {
     if (valid) {
-        __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+        pk_bload16(r, voff, soff, lds_base);
     } else {
         *reinterpret_cast<u4_t*>(lds_base + 16 * lane) = u4_t{0u, 0u, 0u, 0u};
     }
@@ -207,38 +237,38 @@ template <int SCL>
 __device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, int kt, const SuperLoads& L, int lane)
 {
     using namespace pk;
-    const long kb = (long)t * ROWB;
-    const long ks = (long)t * L.sstride;
+    const int kb = t * ROWB;                      // scalar offsets of superstep t
+    const int ks = t * (int)L.sstride;
     if (SCL == SCL_ROW16 || kt == SK) {   // (SCL_ROW16 plans have no short supersteps)
-        __builtin_amdgcn_global_load_lds(L.b[0] + kb, slot_base + L.b_dst[0], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(L.b[1] + kb, slot_base + L.b_dst[1], 16, 0, 0);
+        pk_bload16(L.rb, L.b[0], kb, slot_base + L.b_dst[0]);
+        pk_bload16(L.rb, L.b[1], kb, slot_base + L.b_dst[1]);
         if constexpr (SCL == SCL_ROW16) {
-            if (L.nsb > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 16, 0, 0);
-            if (L.nsa > 0 && lane < 32) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 16, 0, 0);
+            if (L.nsb > 0 && lane < 32) pk_bload16(L.rsb, L.sb, ks, slot_base + L.sb_dst);
+            if (L.nsa > 0 && lane < 32) pk_bload16(L.rsa, L.sa, ks, slot_base + L.sa_dst);
         } else {
-            if (L.nsb > 0) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 4, 0, 0);
-            if (L.nsa > 0) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 4, 0, 0);
+            if (L.nsb > 0) pk_bload4(L.rsb, L.sb, ks, slot_base + L.sb_dst);
+            if (L.nsa > 0) pk_bload4(L.rsa, L.sa, ks, slot_base + L.sa_dst);
         }
-        if (L.na > 0) __builtin_amdgcn_global_load_lds(L.a[0] + kb, slot_base + L.a_dst[0], 16, 0, 0);
-        if (L.na > 1) __builtin_amdgcn_global_load_lds(L.a[1] + kb, slot_base + L.a_dst[1], 16, 0, 0);
+        if (L.na > 0) pk_bload16(L.ra, L.a[0], kb, slot_base + L.a_dst[0]);
+        if (L.na > 1) pk_bload16(L.ra, L.a[1], kb, slot_base + L.a_dst[1]);
     } else {
         // a short last superstep: kt / 32 code chunks and kt / 64 scale dwords per row
         const int vchunks = kt >> 5, vdw = kt >> 6;
-        pk_load16(L.b[0] + kb, slot_base + L.b_dst[0], lane, L.b_chunk[0] < vchunks);
-        pk_load16(L.b[1] + kb, slot_base + L.b_dst[1], lane, L.b_chunk[1] < vchunks);
+        pk_load16(L.rb, L.b[0], kb, slot_base + L.b_dst[0], lane, L.b_chunk[0] < vchunks);
+        pk_load16(L.rb, L.b[1], kb, slot_base + L.b_dst[1], lane, L.b_chunk[1] < vchunks);
         if constexpr (SCL != SCL_ROW16) {
             const bool sv = L.s_dword < vdw;
             if (L.nsb > 0) {
-                if (sv) __builtin_amdgcn_global_load_lds(L.sb + ks, slot_base + L.sb_dst, 4, 0, 0);
+                if (sv) pk_bload4(L.rsb, L.sb, ks, slot_base + L.sb_dst);
                 else *reinterpret_cast<uint32_t*>(slot_base + L.sb_dst + 4 * lane) = 0u;
             }
             if (L.nsa > 0) {
-                if (sv) __builtin_amdgcn_global_load_lds(L.sa + ks, slot_base + L.sa_dst, 4, 0, 0);
+                if (sv) pk_bload4(L.rsa, L.sa, ks, slot_base + L.sa_dst);
                 else *reinterpret_cast<uint32_t*>(slot_base + L.sa_dst + 4 * lane) = 0u;
             }
         }
-        if (L.na > 0) pk_load16(L.a[0] + kb, slot_base + L.a_dst[0], lane, L.a_chunk[0] < vchunks);
-        if (L.na > 1) pk_load16(L.a[1] + kb, slot_base + L.a_dst[1], lane, L.a_chunk[1] < vchunks);
+        if (L.na > 0) pk_load16(L.ra, L.a[0], kb, slot_base + L.a_dst[0], lane, L.a_chunk[0] < vchunks);
+        if (L.na > 1) pk_load16(L.ra, L.a[1], kb, slot_base + L.a_dst[1], lane, L.a_chunk[1] < vchunks);
     }
 }
 
@@ -304,21 +334,45 @@ struct ARaw {
     uint32_t sc[NRB];
 };
 
-template <int NRB, int HALF>
-__device__ __forceinline__ void pk_read_a(ARaw<NRB>& a, const uint8_t* slot_base, int rows, int tid)
+// This lane's byte offsets inside a ring slot (or the A buffer) of every LDS read of the
+// loop, computed once per tile: a read is then the uniform slot base plus one of these plus
+// a compile-time constant (the swizzle depends only on row bits 1..3, so rows 32 apart
+// share it), i.e. one address add per read pattern and superstep.
+struct LdsOffs {
+    int ob[2];    // B codes of half 0 / 1, column block cb0
+    int obs;      // B scale words, column block cb0
+    int oa[2];    // A codes of half 0 / 1, piece 0
+    int osa[2];   // A scale byte of half 0 / 1, piece 0
+};
+
+template <int NRB>
+__device__ __forceinline__ LdsOffs pk_lds_offsets(int lane, int tid, int cw, int tq)
 {
     using namespace pk;
     constexpr int rpad = 32 * NRB;
-    const uint8_t* codes = slot_base + A_CODES_AT;
-    const uint8_t* scales = codes + rpad * ROWB;
+    const int j = lane & 31, h = lane >> 5;
+    const int brow = 64 * cw + j;   // first row of column block cb0 = 2 cw
+    const int r0 = tid >> 4, hp = tid & 15;
+    LdsOffs o;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        o.ob[half] = brow * ROWB + 16 * ((4 * half + 2 * h + (tq >> 1)) ^ swz(brow)) + 8 * (tq & 1);
+        o.oa[half] = A_CODES_AT + r0 * ROWB + 16 * ((4 * half + (hp >> 2)) ^ swz(r0)) + 4 * (hp & 3);
+        o.osa[half] = A_CODES_AT + rpad * ROWB + r0 * SCB + 8 * half + (hp >> 1);
+    }
+    o.obs = B_SCALES_AT + brow * SCB + 4 * h;
+    return o;
+}
+
+// Raw A of half HALF: every thread takes NRB pieces, piece i = rows 32 i further.
+template <int NRB, int HALF>
+__device__ __forceinline__ void pk_read_a(ARaw<NRB>& a, const uint8_t* slot_base, const LdsOffs& o)
+{
+    using namespace pk;
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
-        const int id = tid + THREADS * i;
-        const int r = id >> 4, hp = id & 15;
-        const int chunk = 4 * HALF + (hp >> 2);
-        a.q[i] = *reinterpret_cast<const uint32_t*>(codes + r * ROWB + 16 * (chunk ^ swz(r)) + 4 * (hp & 3));
-        a.sc[i] = scales[r * SCB + 8 * HALF + (hp >> 1)];
-        (void)rows;
+        a.q[i] = *reinterpret_cast<const uint32_t*>(slot_base + o.oa[HALF] + 32 * ROWB * i);
+        a.sc[i] = slot_base[o.osa[HALF] + 32 * SCB * i];
     }
 }
 
@@ -338,25 +392,23 @@ __device__ __forceinline__ void pk_write_a(const ARaw<NRB>& a, uint8_t* dst, int
 // B operand: raw bytes -> registers
 // ---------------------------------------------------------------------------------------
 
-// The lane's 8 B code bytes of half HALF of the superstep in `slot_base`, for the tile's
-// column block c (row 32 c + j): K values 64h + 16t + 8u .. +8 for steps u = 0, 1 (dword u).
+// The lane's 8 B code bytes of half HALF of the superstep in `slot_base`, for column block
+// cb0 + c (row 32 (cb0 + c) + j): chunk 4 HALF + 2h + t / 2 of the row (stored at chunk
+// ^ swz(row)), bytes 8 (t % 2) .. +8, i.e. K values 64h + 16t + 8u .. +8 for steps
+// u = 0, 1 (dword u).
 template <int HALF>
-__device__ __forceinline__ u2_t pk_read_b(const uint8_t* slot_base, int c, int lane, int t)
+__device__ __forceinline__ u2_t pk_read_b(const uint8_t* slot_base, int c, const LdsOffs& o)
 {
     using namespace pk;
-    const int j = lane & 31, h = lane >> 5;
-    const int row = 32 * c + j;
-    const int chunk = 4 * HALF + 2 * h + (t >> 1);
-    return *reinterpret_cast<const u2_t*>(slot_base + row * ROWB + 16 * (chunk ^ swz(row)) + 8 * (t & 1));
+    return *reinterpret_cast<const u2_t*>(slot_base + o.ob[HALF] + 32 * ROWB * c);
 }
 
-// The two scale words of row 32 c + j that this lane needs in a superstep: words h and
-// 2 + h of the row's 16 scale bytes (half 0 and half 1).
-__device__ __forceinline__ u2_t pk_read_bs(const uint8_t* slot_base, int c, int lane)
+// The two scale words of row 32 (cb0 + c) + j that this lane needs in a superstep: words h
+// and 2 + h of the row's 16 scale bytes (half 0 and half 1).
+__device__ __forceinline__ u2_t pk_read_bs(const uint8_t* slot_base, int c, const LdsOffs& o)
 {
     using namespace pk;
-    const uint32_t* w =
-        reinterpret_cast<const uint32_t*>(slot_base + B_SCALES_AT + (32 * c + (lane & 31)) * SCB) + (lane >> 5);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(slot_base + o.obs + 32 * SCB * c);
     return u2_t{w[0], w[2]};
 }
 
@@ -394,8 +446,8 @@ __device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[2][NRB], const h8_t (&bf)
 // alternation with scheduling-group barriers measured 6-10% slower.
 template <int NRB, int HALF>
 __device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], u2_t (&srow)[2], const uint8_t* cur,
-                                        const uint8_t* nxt, const uint8_t* ahalf, uint8_t* anext, int rows,
-                                        uint32_t tsel, int cb0, int lane, int t, int tid)
+                                        const uint8_t* nxt, const uint8_t* ahalf, uint8_t* anext, const LdsOffs& o,
+                                        uint32_t tsel, int tid)
 {
     using namespace pk;
     h8_t af[2][NRB];
@@ -407,15 +459,15 @@ __device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2],
     u2_t qn[2];     // raw B codes of the next half
     ARaw<NRB> an;   // raw A of the next half
     if constexpr (HALF == 0) {
-        qn[0] = pk_read_b<1>(cur, cb0, lane, t);
-        qn[1] = pk_read_b<1>(cur, cb0 + 1, lane, t);
-        pk_read_a<NRB, 1>(an, cur, rows, tid);
+        qn[0] = pk_read_b<1>(cur, 0, o);
+        qn[1] = pk_read_b<1>(cur, 1, o);
+        pk_read_a<NRB, 1>(an, cur, o);
     } else {
-        srow[0] = pk_read_bs(nxt, cb0, lane);
-        srow[1] = pk_read_bs(nxt, cb0 + 1, lane);
-        qn[0] = pk_read_b<0>(nxt, cb0, lane, t);
-        qn[1] = pk_read_b<0>(nxt, cb0 + 1, lane, t);
-        pk_read_a<NRB, 0>(an, nxt, rows, tid);
+        srow[0] = pk_read_bs(nxt, 0, o);
+        srow[1] = pk_read_bs(nxt, 1, o);
+        qn[0] = pk_read_b<0>(nxt, 0, o);
+        qn[1] = pk_read_b<0>(nxt, 1, o);
+        pk_read_a<NRB, 0>(an, nxt, o);
     }
     pk_mfmas<NRB>(acc, bf[0], af[0]);
     pk_mfmas<NRB>(acc, bf[1], af[1]);
@@ -550,11 +602,13 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     SuperLoads L;
     {
         const int rl = lane >> 3, pos = lane & 7;
+        L.bb = G.b + (long)col0 * qs;
+        L.ab = G.a + (long)row0 * qs;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int i = wave + 8 * q;   // B code instruction
             const int r = 8 * i + rl;
-            L.b[q] = G.b + (long)min(col0 + r, n - 1) * qs + 16 * (pos ^ swz(r));
+            L.b[q] = (uint32_t)((long)(min(col0 + r, n - 1) - col0) * qs + 16 * (pos ^ swz(r)));
             L.b_dst[q] = 8 * i * ROWB;
             L.b_chunk[q] = pos ^ swz(r);
         }
@@ -564,7 +618,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         for (int q = 0; q < 2; ++q) {
             const int a = ((wave + 4) & 7) + 8 * q;   // A code instruction
             const int r = 8 * a + rl;
-            L.a[q] = G.a + (long)(row0 + min(r, rows - 1)) * qs + 16 * (pos ^ swz(r));
+            L.a[q] = (uint32_t)((long)min(r, rows - 1) * qs + 16 * (pos ^ swz(r)));
             L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
             L.a_chunk[q] = pos ^ swz(r);
             if (a < na_total) L.na = q + 1;
@@ -576,40 +630,54 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             // the 4 scales of a row in one atom are contiguous.  Lane l of scale instruction
             // q = wave loads the 4 bytes of row 16 q + l / 4 in the superstep's atom l % 4
             // (K blocks 16 t + 4 (l % 4) .. +4), which land at LDS byte 16 (row) + 4 (l % 4).
+            // (bases: the tile's first 128-row block; col0 is a multiple of 128, so all B rows
+            // of the tile sit in that block, A rows in it or the next)
             const long atoms = k / 64;
             const int piece = lane & 3;
             const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
+            L.sbb = G.sfb + (long)(col0 >> 7) * atoms * 512;
             L.nsb = 1;
-            L.sb = G.sfb + ((long)(gb >> 7) * atoms + piece) * 512 + 16 * (gb & 31) + 4 * ((gb >> 5) & 3);
+            L.sb = (uint32_t)((((long)(gb >> 7) - (col0 >> 7)) * atoms + piece) * 512 + 16 * (gb & 31) +
+                              4 * ((gb >> 5) & 3));
             L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
             const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
+            L.sab = G.sfa + (long)(row0 >> 7) * atoms * 512;
             L.nsa = wave < rpad / 16 ? 1 : 0;
-            L.sa = G.sfa + ((long)(ga >> 7) * atoms + piece) * 512 + 16 * (ga & 31) + 4 * ((ga >> 5) & 3);
+            L.sa = (uint32_t)((((long)(ga >> 7) - (row0 >> 7)) * atoms + piece) * 512 + 16 * (ga & 31) +
+                              4 * ((ga >> 5) & 3));
             L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
             L.sstride = 4 * 512;             // four atoms per superstep
         } else if constexpr (SCL == SCL_ROW4) {
             // row-major scales, lane l of scale instruction q = wave: dword l % 4 of the
             // superstep's 16 scale bytes of row 16 q + l / 4
             const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
+            L.sbb = G.sfb + (long)col0 * ss;
             L.nsb = 1;
-            L.sb = G.sfb + (long)gb * ss + 4 * (lane & 3);
+            L.sb = (uint32_t)((long)(gb - col0) * ss + 4 * (lane & 3));
             L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
-            const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
+            const int ga = min(16 * wave + (lane >> 2), rows - 1);
+            L.sab = G.sfa + (long)row0 * ss;
             L.nsa = wave < rpad / 16 ? 1 : 0;
-            L.sa = G.sfa + (long)ga * ss + 4 * (lane & 3);
+            L.sa = (uint32_t)((long)ga * ss + 4 * (lane & 3));
             L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
             L.sstride = SCB;
         } else {
             L.sstride = SCB;
+            L.sbb = G.sfb + (long)col0 * ss;
+            L.sab = G.sfa + (long)row0 * ss;
             L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
-            L.sb = G.sfb + (long)min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) * ss;
+            L.sb = (uint32_t)((long)(min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) - col0) * ss);
             L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
             const int qa = 7 - wave;         // A scale instruction
             L.nsa = qa < rpad / 32 ? 1 : 0;
-            L.sa = G.sfa + (long)(row0 + min(32 * qa + (lane & 31), rows - 1)) * ss;
+            L.sa = (uint32_t)((long)min(32 * qa + (lane & 31), rows - 1) * ss);
             L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
         }
         L.ops = 2 + L.nsb + L.na + L.nsa;
+        L.rb = pk_rsrc(L.bb);
+        L.ra = pk_rsrc(L.ab);
+        L.rsb = pk_rsrc(L.sbb);
+        L.rsa = pk_rsrc(L.sab);
     }
 
     f16v_t acc[2][NRB];
@@ -631,13 +699,13 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     uint8_t* a16h[2] = {a16, a16 + rpad * A_ROW};
     const int aoff = j * A_ROW + 128 * h + 32 * tq;   // this lane's A fragment row
     const uint32_t tsel = 0x0c0c0000u | ((uint32_t)(4 + tq) << 8) | (uint32_t)tq;
-    const int cb0 = 2 * cw;
-    u2_t srow[2] = {pk_read_bs(ring, cb0, lane), pk_read_bs(ring, cb0 + 1, lane)};
+    const LdsOffs lo = pk_lds_offsets<NRB>(lane, tid, cw, tq);
+    u2_t srow[2] = {pk_read_bs(ring, 0, lo), pk_read_bs(ring, 1, lo)};
     h8_t bf[2][2];
     {
-        const u2_t q0 = pk_read_b<0>(ring, cb0, lane, tq), q1 = pk_read_b<0>(ring, cb0 + 1, lane, tq);
+        const u2_t q0 = pk_read_b<0>(ring, 0, lo), q1 = pk_read_b<0>(ring, 1, lo);
         ARaw<NRB> a0;
-        pk_read_a<NRB, 0>(a0, ring, rows, tid);
+        pk_read_a<NRB, 0>(a0, ring, lo);
         const h2_t sc = pk_scales<0>(srow, tsel);
         const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
         bf[0][0] = __builtin_bit_cast(h8_t, dequant8(q0.x, s0));
@@ -663,7 +731,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         // after the last superstep the "next" reads land on a slot that holds no data any
         // more: harmless, and their results are unused
         const uint8_t* nxt = ring + ns * sbytes;
-        pk_half<NRB, 0>(acc, bf, srow, cur, nxt, a16h[0] + aoff, a16h[1], rows, tsel, cb0, lane, tq, tid);
+        pk_half<NRB, 0>(acc, bf, srow, cur, nxt, a16h[0] + aoff, a16h[1], lo, tsel, tid);
         // superstep t + 1 must have landed before half 1 reads its bytes (loads complete in
         // issue order, so later supersteps may stay in flight)
         if (t + nslots - 1 < supers) {
@@ -672,7 +740,7 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
             pk_wait_loads((supers - 2 - t) * L.ops);
         }
         barrier_lds();
-        pk_half<NRB, 1>(acc, bf, srow, cur, nxt, a16h[1] + aoff, a16h[0], rows, tsel, cb0, lane, tq, tid);
+        pk_half<NRB, 1>(acc, bf, srow, cur, nxt, a16h[1] + aoff, a16h[0], lo, tsel, tid);
         barrier_lds();
         cs = ns;
     }
