@@ -72,7 +72,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m precision_moe_nvfp4_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python precision_moe_nvfp4_amd/build.py` "
             "(there is no fallback path)")
     L = ctypes.CDLL(LIB_PATH)
     runtimes = _hip_runtimes_mapped()

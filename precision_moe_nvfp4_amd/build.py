@@ -1,6 +1,7 @@
 """Build the gfx950 shared library libnvfp4gg.so in-tree with hipcc.
 
-Usage: python -m precision_moe_nvfp4_amd.build [-v]
+Usage: python precision_moe_nvfp4_amd/build.py [-v]   (run as a script: importing it through
+the package would first load the library it builds)
 """
 from __future__ import annotations
 

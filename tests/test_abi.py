@@ -191,3 +191,15 @@ def test_k_granularity_and_variant(k, variant):
     # one group with a K tail moves the whole plan to the 4-byte scale variant
     mixed = gg.nvfp4_gg_plan_problems([(10, 64, 512), (10, 64, k)], device=gg.DEVICE_NONE)
     assert gg.nvfp4_gg_plan_info(mixed).variant == (2 if k % 256 == 0 else 4)
+
+
+def test_build_script_loads_without_the_package():
+    """build() must work on a tree where the library is not built yet: the build script is
+    loaded by path and must not import the package (whose __init__ loads the library)."""
+    import subprocess
+    import sys
+    code = ("import sys, __graft_entry__ as g; m = g._hip_build_module(); "
+            "assert callable(m.build); "
+            "assert 'precision_moe_nvfp4_amd' not in sys.modules, 'package imported'")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    subprocess.run([sys.executable, "-c", code], cwd=root, check=True)
