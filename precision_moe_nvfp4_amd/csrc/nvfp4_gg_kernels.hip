@@ -16,23 +16,21 @@
 // Wave w owns the 64 columns 64 (w & 1) .. +64 and all tile rows, and one quarter of every
 // K step (w >> 1); the four partial sums of a column half are added through LDS at the
 // end.  So each dequantised B fragment feeds one MFMA per 32 tile rows, and each A
-// fragment read from LDS feeds two MFMAs:
+// fragment feeds two MFMAs:
 //   * An LDS ring receives, per superstep of K = 256, the raw bytes of the superstep (B
 //     rows, A rows and their scales) straight from HBM through direct-to-LDS loads (no
-//     VGPR staging), one whole 128-byte line per row and load instruction; 3 or 4
-//     supersteps are in flight, as the tile height allows.
-//   * B (the large operand) is dequantised in registers right before its MFMAs.
-//   * A (shared by the waves) is dequantised once per workgroup, by all 8 waves, into a
-//     double-buffered fp16 LDS buffer holding half a superstep (K = 128), one half ahead of
-//     its use, and read back as MFMA fragments.
-//   * The 2 compute steps (K = 64) of a half run without barriers, from B fragments
-//     dequantised during the previous half; the MFMAs are interleaved with the
-//     dequantisation of the next half's operands.
+//     VGPR staging), one whole 128-byte line per row and load instruction; LDS holds
+//     nothing else, so 5 to 7 slots fit and 3 to 5 supersteps stay in flight.
+//   * Every wave reads the raw bytes of its own K quarter of both operands from the ring
+//     and dequantises them in registers into MFMA fragments, one half superstep ahead of
+//     their use, while the MFMAs of the current half run.
+//   * One barrier per superstep both publishes the next superstep's slot and frees the
+//     slot just consumed, which is refilled at once.
 //   * v_mfma_f32_32x32x16_f16 takes the B fragment as its M-side operand, so each lane
 //     ends up holding runs of 4 consecutive C columns (8-byte fp16 stores).
 // K is permuted inside each half superstep, identically for A and B (the dot product is
 // unchanged): lane half h, K quarter t and step u take the 8 K values starting at
-// 64h + 16t + 8u, so that a lane's B bytes of a whole half are 8 contiguous bytes.
+// 64h + 16t + 8u, so that a lane's bytes of a whole half are 8 contiguous bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,14 +53,6 @@ __device__ __forceinline__ uint16_t f16_bits_rne(float f)
 {
     const _Float16 h = (_Float16)f;
     return __builtin_bit_cast(uint16_t, h);
-}
-
-// E4M3FN byte 0 of x -> the fp16 pair (s, s).  The hardware OCP E4M3 conversion with
-// scale 1.0 is exact (every E4M3 value is an fp16 number).
-__device__ __forceinline__ h2_t scale_pair(uint32_t x)
-{
-    const h2_t s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
-    return h2_t{s.x, s.x};
 }
 
 // 8 E2M1 codes (nibble i = element i, i.e. low nibble = even K) times one fp16 scale ->
@@ -88,26 +78,22 @@ constexpr int BN = 128;              // tile columns: wave w owns columns 64 (w 
 constexpr int RMAX = 96;             // tile rows (multiple of 32)
 
 constexpr int SK = 256;              // K per load superstep
-constexpr int HK = SK / 2;           // K per half superstep (one fp16 A buffer)
 constexpr int ROWB = SK / 2;         // code bytes per row and superstep: one 128-byte line
 constexpr int SCB = SK / 16;         // scale bytes per row and superstep
-constexpr int MAX_SLOTS = 4;
+constexpr int MAX_SLOTS = 7;
 constexpr int LDS_BYTES = 160 * 1024;
-// LDS layout of a tile with rpad rows (all offsets multiples of 16 bytes):
-//   [0, 2 * rpad * A_ROW)      fp16 A of two half supersteps (double buffer)
-//   then ring_slots(rpad) slots of slot_bytes(rpad), each holding the raw bytes of one
-//   superstep:
+// LDS holds only the ring: ring_slots(rpad) slots of slot_bytes(rpad) for a tile with rpad
+// rows, each holding the raw bytes of one superstep (all offsets multiples of 16 bytes):
 //     B codes   128 rows x 128 B   at 0            (16-byte chunk c of row r at c ^ swz(r))
 //     B scales  128 rows x 16 B    at B_SCALES_AT
 //     A codes   rpad rows x 128 B  at A_CODES_AT   (same chunk swizzle)
 //     A scales  rpad rows x 16 B   at A_CODES_AT + 128 rpad
-// Whole 128-byte lines per row and load instruction: a wave's 16-byte lanes cover 8 rows
-// per instruction instead of 32, which is what lets a CU pull shared operand rows out of
-// L2 at ~3x the rate of 32-byte row pieces.
-constexpr int A_ROW = HK * 2 + 16;                    // 272 B per fp16 row (spreads banks)
-// Chunk swizzle of the raw rows: the 3-bit reversal of (r >> 1) & 7.  Reads of one chunk
-// from 16 consecutive rows (16 bytes per lane) and reads of half a row from 4 consecutive
-// rows (4 bytes per lane) then hit 64 distinct banks.
+// (5 slots of 96-row tiles, 5 of 64-row tiles, 7 of 32-row tiles).  Whole 128-byte lines
+// per row and load instruction: a wave's 16-byte lanes cover 8 rows per instruction
+// instead of 32, which is what lets a CU pull shared operand rows out of L2 at ~3x the
+// rate of 32-byte row pieces.
+// Chunk swizzle of the raw rows: the 3-bit reversal of (r >> 1) & 7, so that the 8-byte
+// reads of one chunk half from 32 consecutive rows spread over 16 chunk positions.
 __host__ __device__ constexpr int swz(int r)
 {
     return (((r >> 1) & 1) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1);
@@ -115,15 +101,13 @@ __host__ __device__ constexpr int swz(int r)
 constexpr int B_SCALES_AT = BN * ROWB;                // 16384
 constexpr int A_CODES_AT = B_SCALES_AT + BN * SCB;    // 18432
 __host__ __device__ constexpr int slot_bytes(int rpad) { return A_CODES_AT + rpad * (ROWB + SCB); }
-__host__ __device__ constexpr int ring_base(int rpad) { return 2 * rpad * A_ROW; }
 __host__ __device__ constexpr int ring_slots(int rpad)
 {
-    return (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad) > MAX_SLOTS
-               ? MAX_SLOTS
-               : (LDS_BYTES - ring_base(rpad)) / slot_bytes(rpad);
+    return LDS_BYTES / slot_bytes(rpad) > MAX_SLOTS ? MAX_SLOTS : LDS_BYTES / slot_bytes(rpad);
 }
-// reduction area: per wave, for each column block and 32-row block, the three element
-// groups handed to the other K quarters (one u4 per lane each)
+// reduction area (overlays the ring after the last superstep): per wave, for each column
+// block and 32-row block, the three element groups handed to the other K quarters (one u4
+// per lane each)
 constexpr int RED_WAVE = 2 * (RMAX / 32) * 3 * 64 * 16;
 static_assert(ring_slots(RMAX) >= 3, "the tallest tile needs at least 3 ring slots");
 static_assert(8 * RED_WAVE <= LDS_BYTES, "reduction area must fit in LDS");
@@ -291,25 +275,6 @@ __device__ __forceinline__ void pk_wait_loads(int n)
 #undef NVFP4GG_WAIT_CASE
 }
 
-// The same wait for the steady state of the ring, where a wave's count is one of two values
-// for a given tile height and scale layout (its share of the loads times the supersteps
-// left in flight): one uniform branch instead of a search over every count.
-template <int NRB, int SCL>
-__device__ __forceinline__ void pk_wait_steady(int n)
-{
-    constexpr bool B4 = SCL != SCL_ROW16;
-    constexpr int AHEAD = pk::ring_slots(32 * NRB) - 2;
-    constexpr int LO = AHEAD * pk_ops_min(NRB, B4), HI = AHEAD * pk_ops_max(NRB, B4);
-    static_assert(HI <= 15, "the constant waits use the 4 low vmcnt bits");
-    if (n == HI) {
-        __builtin_amdgcn_s_waitcnt(0x0f70 | HI);   // vmcnt(HI); expcnt and lgkmcnt not waited for
-    } else if (n == LO) {
-        __builtin_amdgcn_s_waitcnt(0x0f70 | LO);
-    } else {
-        pk_wait_loads(n);
-    }
-}
-
 // Workgroup barrier for LDS hand-offs: waits for this wave's own LDS reads/writes, then
 // s_barrier.  Unlike __syncthreads() it does not wait for outstanding direct-to-LDS
 // loads (those are waited for explicitly, so later supersteps stay in flight).
@@ -319,98 +284,8 @@ __device__ __forceinline__ void barrier_lds()
 }
 
 // ---------------------------------------------------------------------------------------
-// A operand: raw bytes -> fp16 LDS buffer
+// Scales
 // ---------------------------------------------------------------------------------------
-
-// Dequantisation of half HALF of the superstep held in a ring slot into one fp16 buffer
-// (natural K order, A_ROW-byte rows), all 8 waves together, split into a read (issued
-// early) and the conversion and store (whose VALU work then overlaps MFMAs).  Every
-// thread takes NRB pieces: piece id = tid + 512 i covers row id / 16, K values 8 (id % 16)
-// .. +8 of the half (4 code bytes; one scale byte).  Rows in [rows, rpad) repeat the last
-// row (the loads clamp to it); their results land in tile rows that are never stored.
-template <int NRB>
-struct ARaw {
-    uint32_t q[NRB];
-    uint32_t sc[NRB];
-};
-
-// This lane's byte offsets inside a ring slot (or the A buffer) of every LDS read of the
-// loop, computed once per tile: a read is then the uniform slot base plus one of these plus
-// a compile-time constant (the swizzle depends only on row bits 1..3, so rows 32 apart
-// share it), i.e. one address add per read pattern and superstep.
-struct LdsOffs {
-    int ob[2];    // B codes of half 0 / 1, column block cb0
-    int obs;      // B scale words, column block cb0
-    int oa[2];    // A codes of half 0 / 1, piece 0
-    int osa[2];   // A scale byte of half 0 / 1, piece 0
-};
-
-template <int NRB>
-__device__ __forceinline__ LdsOffs pk_lds_offsets(int lane, int tid, int cw, int tq)
-{
-    using namespace pk;
-    constexpr int rpad = 32 * NRB;
-    const int j = lane & 31, h = lane >> 5;
-    const int brow = 64 * cw + j;   // first row of column block cb0 = 2 cw
-    const int r0 = tid >> 4, hp = tid & 15;
-    LdsOffs o;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        o.ob[half] = brow * ROWB + 16 * ((4 * half + 2 * h + (tq >> 1)) ^ swz(brow)) + 8 * (tq & 1);
-        o.oa[half] = A_CODES_AT + r0 * ROWB + 16 * ((4 * half + (hp >> 2)) ^ swz(r0)) + 4 * (hp & 3);
-        o.osa[half] = A_CODES_AT + rpad * ROWB + r0 * SCB + 8 * half + (hp >> 1);
-    }
-    o.obs = B_SCALES_AT + brow * SCB + 4 * h;
-    return o;
-}
-
-// Raw A of half HALF: every thread takes NRB pieces, piece i = rows 32 i further.
-template <int NRB, int HALF>
-__device__ __forceinline__ void pk_read_a(ARaw<NRB>& a, const uint8_t* slot_base, const LdsOffs& o)
-{
-    using namespace pk;
-#pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-        a.q[i] = *reinterpret_cast<const uint32_t*>(slot_base + o.oa[HALF] + 32 * ROWB * i);
-        a.sc[i] = slot_base[o.osa[HALF] + 32 * SCB * i];
-    }
-}
-
-template <int NRB>
-__device__ __forceinline__ void pk_write_a(const ARaw<NRB>& a, uint8_t* dst, int tid)
-{
-    using namespace pk;
-#pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-        const int id = tid + THREADS * i;
-        const int r = id >> 4, hp = id & 15;
-        *reinterpret_cast<u4_t*>(dst + r * A_ROW + 16 * hp) = dequant8(a.q[i], scale_pair(a.sc[i]));
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// B operand: raw bytes -> registers
-// ---------------------------------------------------------------------------------------
-
-// The lane's 8 B code bytes of half HALF of the superstep in `slot_base`, for column block
-// cb0 + c (row 32 (cb0 + c) + j): chunk 4 HALF + 2h + t / 2 of the row (stored at chunk
-// ^ swz(row)), bytes 8 (t % 2) .. +8, i.e. K values 64h + 16t + 8u .. +8 for steps
-// u = 0, 1 (dword u).
-template <int HALF>
-__device__ __forceinline__ u2_t pk_read_b(const uint8_t* slot_base, int c, const LdsOffs& o)
-{
-    using namespace pk;
-    return *reinterpret_cast<const u2_t*>(slot_base + o.ob[HALF] + 32 * ROWB * c);
-}
-
-// The two scale words of row 32 (cb0 + c) + j that this lane needs in a superstep: words h
-// and 2 + h of the row's 16 scale bytes (half 0 and half 1).
-__device__ __forceinline__ u2_t pk_read_bs(const uint8_t* slot_base, int c, const LdsOffs& o)
-{
-    using namespace pk;
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(slot_base + o.obs + 32 * SCB * c);
-    return u2_t{w[0], w[2]};
-}
 
 // fp16 scale pair (column block 0, column block 1) of half HALF: byte 8 HALF + 4h + t of
 // each row's scale bytes, i.e. byte t of the lane's word for that half.
@@ -434,50 +309,6 @@ __device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[2][NRB], const h8_t (&bf)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
             acc[c][rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c], af[rb], acc[c][rb], 0, 0, 0);
-}
-
-// One half superstep (steps u = 0, 1 of half HALF of the superstep in `cur`, A in the fp16
-// buffer at `ahalf`, B fragments bf[u][c] dequantised during the previous half).  While its
-// MFMAs run, the next half's B fragments are dequantised into bf (from half 1 of `cur`, or
-// half 0 of the next superstep `nxt`, whose scale rows replace `srow` when HALF = 1) and
-// the next half of A into `anext` (all threads share that work), so that no MFMA waits
-// for VALU work of its own half.  The LDS reads come first.  The compiler's own schedule
-// of the independent MFMA and VALU streams is kept: forcing a strict MFMA/VALU
-// alternation with scheduling-group barriers measured 6-10% slower.
-template <int NRB, int HALF>
-__device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], u2_t (&srow)[2], const uint8_t* cur,
-                                        const uint8_t* nxt, const uint8_t* ahalf, uint8_t* anext, const LdsOffs& o,
-                                        uint32_t tsel, int tid)
-{
-    using namespace pk;
-    h8_t af[2][NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-        af[0][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW);
-        af[1][rb] = *reinterpret_cast<const h8_t*>(ahalf + rb * 32 * A_ROW + 16);
-    }
-    u2_t qn[2];     // raw B codes of the next half
-    ARaw<NRB> an;   // raw A of the next half
-    if constexpr (HALF == 0) {
-        qn[0] = pk_read_b<1>(cur, 0, o);
-        qn[1] = pk_read_b<1>(cur, 1, o);
-        pk_read_a<NRB, 1>(an, cur, o);
-    } else {
-        srow[0] = pk_read_bs(nxt, 0, o);
-        srow[1] = pk_read_bs(nxt, 1, o);
-        qn[0] = pk_read_b<0>(nxt, 0, o);
-        qn[1] = pk_read_b<0>(nxt, 1, o);
-        pk_read_a<NRB, 0>(an, nxt, o);
-    }
-    pk_mfmas<NRB>(acc, bf[0], af[0]);
-    pk_mfmas<NRB>(acc, bf[1], af[1]);
-    const h2_t sc = pk_scales<1 - HALF>(srow, tsel);
-    const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
-    pk_write_a<NRB>(an, anext, tid);
-    bf[0][0] = __builtin_bit_cast(h8_t, dequant8(qn[0].x, s0));
-    bf[0][1] = __builtin_bit_cast(h8_t, dequant8(qn[1].x, s1));
-    bf[1][0] = __builtin_bit_cast(h8_t, dequant8(qn[0].y, s0));
-    bf[1][1] = __builtin_bit_cast(h8_t, dequant8(qn[1].y, s1));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -571,114 +402,259 @@ __device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uin
 // Tile
 // ---------------------------------------------------------------------------------------
 
-// One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)).  All
-// 8 waves execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs
-// per B fragment; SCL is how the scales are fetched (ScaleMode).  K is a multiple of 64;
-// the last superstep holds k - 256 (supers - 1) K values.
-template <int NRB, int SCL>
-__device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_, uint8_t* smem)
+// This wave's loads of a tile (see SuperLoads): lane l of a code instruction covers row
+// (first row + l / 8) and stores LDS chunk l % 8, which holds global chunk (l % 8) ^ swz(row).
+template <int SCL>
+__device__ __forceinline__ SuperLoads pk_super_loads(const GroupArgs& G, int n, int k, int row0, int rows, int col0,
+                                                     int rpad, int wave, int lane)
 {
     using namespace pk;
-    // workgroup-uniform scalars (the call passes them in vector registers)
+    const long qs = k / 2, ss = k / 16;
+    SuperLoads L;
+    const int rl = lane >> 3, pos = lane & 7;
+    L.bb = G.b + (long)col0 * qs;
+    L.ab = G.a + (long)row0 * qs;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = wave + 8 * q;   // B code instruction
+        const int r = 8 * i + rl;
+        L.b[q] = (uint32_t)((long)(min(col0 + r, n - 1) - col0) * qs + 16 * (pos ^ swz(r)));
+        L.b_dst[q] = 8 * i * ROWB;
+        L.b_chunk[q] = pos ^ swz(r);
+    }
+    const int na_total = rpad / 8;
+    L.na = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int a = ((wave + 4) & 7) + 8 * q;   // A code instruction
+        const int r = 8 * a + rl;
+        L.a[q] = (uint32_t)((long)min(r, rows - 1) * qs + 16 * (pos ^ swz(r)));
+        L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
+        L.a_chunk[q] = pos ^ swz(r);
+        if (a < na_total) L.na = q + 1;
+    }
+    L.s_dword = lane & 3;
+    if constexpr (SCL == SCL_BLOCKED) {
+        // 128x4 blocked scales: the scale of (row r, K block c) sits in 512-byte atom
+        // (r / 128) * (k / 64) + c / 4 at byte 16 (r % 32) + 4 ((r / 32) % 4) + c % 4, so
+        // the 4 scales of a row in one atom are contiguous.  Lane l of scale instruction
+        // q = wave loads the 4 bytes of row 16 q + l / 4 in the superstep's atom l % 4
+        // (K blocks 16 t + 4 (l % 4) .. +4), which land at LDS byte 16 (row) + 4 (l % 4).
+        // (bases: the tile's first 128-row block; col0 is a multiple of 128, so all B rows
+        // of the tile sit in that block, A rows in it or the next)
+        const long atoms = k / 64;
+        const int piece = lane & 3;
+        const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
+        L.sbb = G.sfb + (long)(col0 >> 7) * atoms * 512;
+        L.nsb = 1;
+        L.sb = (uint32_t)((((long)(gb >> 7) - (col0 >> 7)) * atoms + piece) * 512 + 16 * (gb & 31) +
+                          4 * ((gb >> 5) & 3));
+        L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
+        const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
+        L.sab = G.sfa + (long)(row0 >> 7) * atoms * 512;
+        L.nsa = wave < rpad / 16 ? 1 : 0;
+        L.sa = (uint32_t)((((long)(ga >> 7) - (row0 >> 7)) * atoms + piece) * 512 + 16 * (ga & 31) +
+                          4 * ((ga >> 5) & 3));
+        L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
+        L.sstride = 4 * 512;             // four atoms per superstep
+    } else if constexpr (SCL == SCL_ROW4) {
+        // row-major scales, lane l of scale instruction q = wave: dword l % 4 of the
+        // superstep's 16 scale bytes of row 16 q + l / 4
+        const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
+        L.sbb = G.sfb + (long)col0 * ss;
+        L.nsb = 1;
+        L.sb = (uint32_t)((long)(gb - col0) * ss + 4 * (lane & 3));
+        L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
+        const int ga = min(16 * wave + (lane >> 2), rows - 1);
+        L.sab = G.sfa + (long)row0 * ss;
+        L.nsa = wave < rpad / 16 ? 1 : 0;
+        L.sa = (uint32_t)((long)ga * ss + 4 * (lane & 3));
+        L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
+        L.sstride = SCB;
+    } else {
+        L.sstride = SCB;
+        L.sbb = G.sfb + (long)col0 * ss;
+        L.sab = G.sfa + (long)row0 * ss;
+        L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
+        L.sb = (uint32_t)((long)(min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) - col0) * ss);
+        L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
+        const int qa = 7 - wave;         // A scale instruction
+        L.nsa = qa < rpad / 32 ? 1 : 0;
+        L.sa = (uint32_t)((long)min(32 * qa + (lane & 31), rows - 1) * ss);
+        L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
+    }
+    L.ops = 2 + L.nsb + L.na + L.nsa;
+    L.rb = pk_rsrc(L.bb);
+    L.ra = pk_rsrc(L.ab);
+    L.rsb = pk_rsrc(L.sbb);
+    L.rsa = pk_rsrc(L.sab);
+    return L;
+}
+
+// ---------------------------------------------------------------------------------------
+// Tile
+// ---------------------------------------------------------------------------------------
+//
+// Every wave reads the raw A bytes of its own K quarter for all tile rows straight from the
+// ring slot, exactly as it reads its B bytes, and dequantises both into MFMA fragments in
+// registers.  The two column halves thus both convert the A rows (a shared fp16 A buffer in
+// LDS would convert them once), which measured cheaper than that buffer's LDS writes,
+// fragment reads and second barrier per superstep; the LDS it would take holds more ring
+// slots instead.
+
+// This lane's LDS byte offsets inside a ring slot: raw codes of half 0 / 1 (column block
+// cb0, row block 0) and the scale words, for B and A.  Both operands use the same lane
+// mapping (lane (j, h), K quarter tq: row j of a 32-row block, chunk 4 half + 2h + tq / 2,
+// bytes 8 (tq % 2) .. +8), and rows 32 apart share the chunk swizzle.
+struct LdsOffs {
+    int ob[2];
+    int oa[2];
+    int obs;
+    int osa;
+};
+
+template <int NRB>
+__device__ __forceinline__ LdsOffs pk_lds_offsets(int lane, int cw, int tq)
+{
+    using namespace pk;
+    const int j = lane & 31, h = lane >> 5;
+    const int brow = 64 * cw + j;
+    LdsOffs o;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int chunk = 4 * half + 2 * h + (tq >> 1);
+        o.ob[half] = brow * ROWB + 16 * (chunk ^ swz(brow)) + 8 * (tq & 1);
+        o.oa[half] = A_CODES_AT + j * ROWB + 16 * (chunk ^ swz(j)) + 8 * (tq & 1);
+    }
+    o.obs = B_SCALES_AT + brow * SCB + 4 * h;
+    o.osa = A_CODES_AT + 32 * NRB * ROWB + j * SCB + 4 * h;
+    return o;
+}
+
+// Raw bytes of half HALF: 8 code bytes (steps u = 0, 1 in dwords x, y) of B column block c
+// or A row block rb.
+template <int HALF>
+__device__ __forceinline__ u2_t pk_rd_b(const uint8_t* slot, int c, const LdsOffs& o)
+{
+    return *reinterpret_cast<const u2_t*>(slot + o.ob[HALF] + 32 * pk::ROWB * c);
+}
+template <int HALF>
+__device__ __forceinline__ u2_t pk_rd_a(const uint8_t* slot, int rb, const LdsOffs& o)
+{
+    return *reinterpret_cast<const u2_t*>(slot + o.oa[HALF] + 32 * pk::ROWB * rb);
+}
+// The two scale words of a row that the lane needs in a superstep: words h (half 0) and
+// 2 + h (half 1) of the row's 16 scale bytes; byte tq of a word is the lane's scale.
+__device__ __forceinline__ u2_t pk_rd_s(const uint8_t* slot, int off)
+{
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(slot + off);
+    return u2_t{w[0], w[2]};
+}
+
+// Dequantise the raw bytes of half HALF into the MFMA fragments bf[u][c] and af[u][rb].
+template <int NRB, int HALF>
+__device__ __forceinline__ void pk_dequant(h8_t (&bf)[2][2], h8_t (&af)[2][NRB], const u2_t (&qb)[2],
+                                             const u2_t (&qa)[NRB], const u2_t (&srow)[2], const u2_t (&arow)[NRB],
+                                             uint32_t tsel)
+{
+    const h2_t sc = pk_scales<HALF>(srow, tsel);
+    const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
+    bf[0][0] = __builtin_bit_cast(h8_t, dequant8(qb[0].x, s0));
+    bf[1][0] = __builtin_bit_cast(h8_t, dequant8(qb[0].y, s0));
+    bf[0][1] = __builtin_bit_cast(h8_t, dequant8(qb[1].x, s1));
+    bf[1][1] = __builtin_bit_cast(h8_t, dequant8(qb[1].y, s1));
+#pragma unroll
+    for (int rb = 0; rb < NRB; rb += 2) {
+        const int r1 = rb + 1 < NRB ? rb + 1 : rb;
+        const h2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(arow[r1][HALF], arow[rb][HALF], tsel),
+                                                                 1.0f, false);
+        const h2_t a0 = {sa.x, sa.x};
+        af[0][rb] = __builtin_bit_cast(h8_t, dequant8(qa[rb].x, a0));
+        af[1][rb] = __builtin_bit_cast(h8_t, dequant8(qa[rb].y, a0));
+        if (rb + 1 < NRB) {
+            const h2_t a1 = {sa.y, sa.y};
+            af[0][rb + 1] = __builtin_bit_cast(h8_t, dequant8(qa[rb + 1].x, a1));
+            af[1][rb + 1] = __builtin_bit_cast(h8_t, dequant8(qa[rb + 1].y, a1));
+        }
+    }
+}
+
+// One half superstep: the MFMAs of half HALF of the superstep in `cur` (fragments bf, af
+// dequantised during the previous half), then the next half's fragments: half 1 of `cur`,
+// or half 0 of the next superstep `nxt`, whose scale words replace srow / arow.  The LDS
+// reads are issued first; the conversions of the next half do not depend on the MFMAs.
+template <int NRB, int HALF>
+__device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], h8_t (&af)[2][NRB], u2_t (&srow)[2],
+                                          u2_t (&arow)[NRB], const uint8_t* cur, const uint8_t* nxt, const LdsOffs& o,
+                                          uint32_t tsel)
+{
+    using namespace pk;
+    u2_t qb[2], qa[NRB];
+    if constexpr (HALF == 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) qb[c] = pk_rd_b<1>(cur, c, o);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) qa[rb] = pk_rd_a<1>(cur, rb, o);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) srow[c] = pk_rd_s(nxt, o.obs + 32 * SCB * c);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) arow[rb] = pk_rd_s(nxt, o.osa + 32 * SCB * rb);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) qb[c] = pk_rd_b<0>(nxt, c, o);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) qa[rb] = pk_rd_a<0>(nxt, rb, o);
+    }
+    pk_mfmas<NRB>(acc, bf[0], af[0]);
+    pk_mfmas<NRB>(acc, bf[1], af[1]);
+    pk_dequant<NRB, 1 - HALF>(bf, af, qb, qa, srow, arow, tsel);
+}
+
+// The steady-state load wait of the ring above: AHEAD = slots - 2 supersteps stay in flight.
+template <int NRB, int SCL>
+__device__ __forceinline__ void pk_wait_steady(int n)
+{
+    constexpr bool B4 = SCL != SCL_ROW16;
+    constexpr int AHEAD = pk::ring_slots(32 * NRB) - 2;
+    constexpr int LO = AHEAD * pk_ops_min(NRB, B4), HI = AHEAD * pk_ops_max(NRB, B4);
+    static_assert(HI <= 63, "vmcnt has 6 bits");
+    // s_waitcnt: vmcnt bits 3..0 and 15..14; expcnt (6..4) and lgkmcnt (11..8) not waited for
+    constexpr int EHI = 0x0f70 | (HI & 15) | ((HI >> 4) << 14);
+    constexpr int ELO = 0x0f70 | (LO & 15) | ((LO >> 4) << 14);
+    if (n == HI) {
+        __builtin_amdgcn_s_waitcnt(EHI);
+    } else if (n == LO) {
+        __builtin_amdgcn_s_waitcnt(ELO);
+    } else {
+        pk_wait_loads(n);
+    }
+}
+
+// One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)), K a
+// multiple of 64 (the last superstep holds k - 256 (supers - 1) K values).  All 8 waves
+// execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs per B
+// fragment; SCL is how the scales are fetched (ScaleMode).  In superstep t, half 0
+// computes and converts half 1 of slot t; then the wave waits for its own loads of
+// superstep t + 1, and the barrier both publishes superstep t + 1 and frees slot t (no
+// wave reads it any more), which is refilled at once with superstep t + slots; half 1
+// computes and converts half 0 of superstep t + 1.
+template <int NRB, int SCL>
+__device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_,
+                                        uint8_t* smem)
+{
+    using namespace pk;
     const int n = __builtin_amdgcn_readfirstlane(n_), k = __builtin_amdgcn_readfirstlane(k_);
     const int row0 = __builtin_amdgcn_readfirstlane(row0_), rows = __builtin_amdgcn_readfirstlane(rows_);
     const int col0 = __builtin_amdgcn_readfirstlane(col0_);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cw = wave & 1, tq = wave >> 1;   // column half, K quarter
-    const int j = lane & 31, h = lane >> 5;
+    const int cw = wave & 1, tq = wave >> 1;
     const int rpad = 32 * NRB;
     const int supers = (k + SK - 1) / SK;
-    const int klast = k - SK * (supers - 1);   // K values of the last superstep
-    const long qs = k / 2, ss = k / 16;
-
+    const int klast = k - SK * (supers - 1);
     const int sbytes = slot_bytes(rpad), nslots = ring_slots(rpad);
-    uint8_t* a16 = smem;
-    uint8_t* ring = smem + ring_base(rpad);
-
-    // this wave's loads (see SuperLoads); lane l of a code instruction covers row
-    // (first row + l / 8) and stores LDS chunk l % 8, which holds global chunk
-    // (l % 8) ^ swz(row)
-    SuperLoads L;
-    {
-        const int rl = lane >> 3, pos = lane & 7;
-        L.bb = G.b + (long)col0 * qs;
-        L.ab = G.a + (long)row0 * qs;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int i = wave + 8 * q;   // B code instruction
-            const int r = 8 * i + rl;
-            L.b[q] = (uint32_t)((long)(min(col0 + r, n - 1) - col0) * qs + 16 * (pos ^ swz(r)));
-            L.b_dst[q] = 8 * i * ROWB;
-            L.b_chunk[q] = pos ^ swz(r);
-        }
-        const int na_total = rpad / 8;
-        L.na = 0;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int a = ((wave + 4) & 7) + 8 * q;   // A code instruction
-            const int r = 8 * a + rl;
-            L.a[q] = (uint32_t)((long)min(r, rows - 1) * qs + 16 * (pos ^ swz(r)));
-            L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
-            L.a_chunk[q] = pos ^ swz(r);
-            if (a < na_total) L.na = q + 1;
-        }
-        L.s_dword = lane & 3;
-        if constexpr (SCL == SCL_BLOCKED) {
-            // 128x4 blocked scales: the scale of (row r, K block c) sits in 512-byte atom
-            // (r / 128) * (k / 64) + c / 4 at byte 16 (r % 32) + 4 ((r / 32) % 4) + c % 4, so
-            // the 4 scales of a row in one atom are contiguous.  Lane l of scale instruction
-            // q = wave loads the 4 bytes of row 16 q + l / 4 in the superstep's atom l % 4
-            // (K blocks 16 t + 4 (l % 4) .. +4), which land at LDS byte 16 (row) + 4 (l % 4).
-            // (bases: the tile's first 128-row block; col0 is a multiple of 128, so all B rows
-            // of the tile sit in that block, A rows in it or the next)
-            const long atoms = k / 64;
-            const int piece = lane & 3;
-            const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
-            L.sbb = G.sfb + (long)(col0 >> 7) * atoms * 512;
-            L.nsb = 1;
-            L.sb = (uint32_t)((((long)(gb >> 7) - (col0 >> 7)) * atoms + piece) * 512 + 16 * (gb & 31) +
-                              4 * ((gb >> 5) & 3));
-            L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
-            const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
-            L.sab = G.sfa + (long)(row0 >> 7) * atoms * 512;
-            L.nsa = wave < rpad / 16 ? 1 : 0;
-            L.sa = (uint32_t)((((long)(ga >> 7) - (row0 >> 7)) * atoms + piece) * 512 + 16 * (ga & 31) +
-                              4 * ((ga >> 5) & 3));
-            L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
-            L.sstride = 4 * 512;             // four atoms per superstep
-        } else if constexpr (SCL == SCL_ROW4) {
-            // row-major scales, lane l of scale instruction q = wave: dword l % 4 of the
-            // superstep's 16 scale bytes of row 16 q + l / 4
-            const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
-            L.sbb = G.sfb + (long)col0 * ss;
-            L.nsb = 1;
-            L.sb = (uint32_t)((long)(gb - col0) * ss + 4 * (lane & 3));
-            L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
-            const int ga = min(16 * wave + (lane >> 2), rows - 1);
-            L.sab = G.sfa + (long)row0 * ss;
-            L.nsa = wave < rpad / 16 ? 1 : 0;
-            L.sa = (uint32_t)((long)ga * ss + 4 * (lane & 3));
-            L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
-            L.sstride = SCB;
-        } else {
-            L.sstride = SCB;
-            L.sbb = G.sfb + (long)col0 * ss;
-            L.sab = G.sfa + (long)row0 * ss;
-            L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
-            L.sb = (uint32_t)((long)(min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) - col0) * ss);
-            L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
-            const int qa = 7 - wave;         // A scale instruction
-            L.nsa = qa < rpad / 32 ? 1 : 0;
-            L.sa = (uint32_t)((long)min(32 * qa + (lane & 31), rows - 1) * ss);
-            L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
-        }
-        L.ops = 2 + L.nsb + L.na + L.nsa;
-        L.rb = pk_rsrc(L.bb);
-        L.ra = pk_rsrc(L.ab);
-        L.rsb = pk_rsrc(L.sbb);
-        L.rsa = pk_rsrc(L.sab);
-    }
+    uint8_t* ring = smem;
+    const SuperLoads L = pk_super_loads<SCL>(G, n, k, row0, rows, col0, rpad, wave, lane);
 
     f16v_t acc[2][NRB];
 #pragma unroll
@@ -686,70 +662,57 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) acc[c][rb] = f16v_t{};
 
-    // prologue: superstep 0 first, on its own, so that it does not queue behind the others
-    // in a memory system that every CU floods at the same moment; then supersteps
-    // 1 .. nslots-1; dequantise the A of superstep 0's first half and read the raw B
-    // operand of its first step
+    // prologue: superstep 0 on its own, then supersteps 1 .. slots-1; convert half 0 of
+    // superstep 0
     const int first = min(nslots, supers);
     const auto kt_of = [&](int t) { return t == supers - 1 ? klast : SK; };
     pk_issue<SCL>(ring, 0, kt_of(0), L, lane);
     pk_wait_loads(0);
     for (int t = 1; t < first; ++t) pk_issue<SCL>(ring + t * sbytes, t, kt_of(t), L, lane);
     barrier_lds();
-    uint8_t* a16h[2] = {a16, a16 + rpad * A_ROW};
-    const int aoff = j * A_ROW + 128 * h + 32 * tq;   // this lane's A fragment row
     const uint32_t tsel = 0x0c0c0000u | ((uint32_t)(4 + tq) << 8) | (uint32_t)tq;
-    const LdsOffs lo = pk_lds_offsets<NRB>(lane, tid, cw, tq);
-    u2_t srow[2] = {pk_read_bs(ring, 0, lo), pk_read_bs(ring, 1, lo)};
-    h8_t bf[2][2];
+    const LdsOffs lo = pk_lds_offsets<NRB>(lane, cw, tq);
+    u2_t srow[2], arow[NRB];
+    h8_t bf[2][2], af[2][NRB];
     {
-        const u2_t q0 = pk_read_b<0>(ring, 0, lo), q1 = pk_read_b<0>(ring, 1, lo);
-        ARaw<NRB> a0;
-        pk_read_a<NRB, 0>(a0, ring, lo);
-        const h2_t sc = pk_scales<0>(srow, tsel);
-        const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
-        bf[0][0] = __builtin_bit_cast(h8_t, dequant8(q0.x, s0));
-        bf[0][1] = __builtin_bit_cast(h8_t, dequant8(q1.x, s1));
-        bf[1][0] = __builtin_bit_cast(h8_t, dequant8(q0.y, s0));
-        bf[1][1] = __builtin_bit_cast(h8_t, dequant8(q1.y, s1));
-        pk_write_a<NRB>(a0, a16h[0], tid);
-    }
-    barrier_lds();
-
-    // loads this wave may leave in flight at the mid-superstep wait while the ring is full
-    const int wait_steady = (nslots - 2) * L.ops;
-    int cs = 0;   // slot of superstep t
-    for (int t = 0; t < supers; ++t) {
-        // the slot of superstep t - 1 is free since the last barrier: refill it with
-        // superstep t - 1 + nslots
-        if (t > 0 && t - 1 + nslots < supers) {
-            const int fs = (cs == 0) ? nslots - 1 : cs - 1;
-            pk_issue<SCL>(ring + fs * sbytes, t - 1 + nslots, kt_of(t - 1 + nslots), L, lane);
+        u2_t qb[2], qa[NRB];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            srow[c] = pk_rd_s(ring, lo.obs + 32 * SCB * c);
+            qb[c] = pk_rd_b<0>(ring, c, lo);
         }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            arow[rb] = pk_rd_s(ring, lo.osa + 32 * SCB * rb);
+            qa[rb] = pk_rd_a<0>(ring, rb, lo);
+        }
+        pk_dequant<NRB, 0>(bf, af, qb, qa, srow, arow, tsel);
+    }
+
+    const int wait_steady = (nslots - 2) * L.ops;
+    int cs = 0;
+    for (int t = 0; t < supers; ++t) {
         const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
         const uint8_t* cur = ring + cs * sbytes;
         // after the last superstep the "next" reads land on a slot that holds no data any
         // more: harmless, and their results are unused
         const uint8_t* nxt = ring + ns * sbytes;
-        pk_half<NRB, 0>(acc, bf, srow, cur, nxt, a16h[0] + aoff, a16h[1], lo, tsel, tid);
-        // superstep t + 1 must have landed before half 1 reads its bytes (loads complete in
-        // issue order, so later supersteps may stay in flight)
+        pk_half<NRB, 0>(acc, bf, af, srow, arow, cur, nxt, lo, tsel);
         if (t + nslots - 1 < supers) {
-            pk_wait_steady<NRB, SCL>(wait_steady);   // supersteps t + 2 .. t + nslots - 1 in flight
+            pk_wait_steady<NRB, SCL>(wait_steady);   // supersteps t + 2 .. t + slots - 1 in flight
         } else if (t + 1 < supers) {
             pk_wait_loads((supers - 2 - t) * L.ops);
         }
         barrier_lds();
-        pk_half<NRB, 1>(acc, bf, srow, cur, nxt, a16h[1] + aoff, a16h[0], lo, tsel, tid);
-        barrier_lds();
+        if (t + nslots < supers) pk_issue<SCL>(ring + cs * sbytes, t + nslots, kt_of(t + nslots), L, lane);
+        pk_half<NRB, 1>(acc, bf, af, srow, arow, cur, nxt, lo, tsel);
         cs = ns;
     }
-
-    // all loads have landed (the last superstep was waited for) and no wave reads the ring
-    // any more: the reduction area may overwrite it
+    // every ring read has completed and every load has landed before the reduction area
+    // overwrites the ring
+    barrier_lds();
     const int ldc = __builtin_amdgcn_readfirstlane(G.ldc);
     pk_reduce_store<NRB>(acc, smem, G.c + (long)row0 * ldc, n, ldc, rows, col0, wave, lane);
-    // the next tile's loads reuse the LDS just read
     barrier_lds();
 }
 
