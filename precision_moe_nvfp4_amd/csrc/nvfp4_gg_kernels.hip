@@ -579,35 +579,63 @@ __device__ __forceinline__ void pk_dequant(h8_t (&bf)[2][2], h8_t (&af)[2][NRB],
     }
 }
 
-// One half superstep: the MFMAs of half HALF of the superstep in `cur` (fragments bf, af
-// dequantised during the previous half), then the next half's fragments: half 1 of `cur`,
-// or half 0 of the next superstep `nxt`, whose scale words replace srow / arow.  The LDS
-// reads are issued first; the conversions of the next half do not depend on the MFMAs.
+// Raw operand bytes of one half superstep in registers: B code bytes of the two column
+// blocks, A code bytes of the row blocks.  Scale words of one superstep: B column blocks,
+// A row blocks.
+template <int NRB>
+struct RawHalf {
+    u2_t b[2];
+    u2_t a[NRB];
+};
+template <int NRB>
+struct ScaleWords {
+    u2_t b[2];
+    u2_t a[NRB];
+};
+
 template <int NRB, int HALF>
-__device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], h8_t (&af)[2][NRB], u2_t (&srow)[2],
-                                          u2_t (&arow)[NRB], const uint8_t* cur, const uint8_t* nxt, const LdsOffs& o,
-                                          uint32_t tsel)
+__device__ __forceinline__ void pk_read_raw(RawHalf<NRB>& q, const uint8_t* slot, const LdsOffs& o)
 {
-    using namespace pk;
-    u2_t qb[2], qa[NRB];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) q.b[c] = pk_rd_b<HALF>(slot, c, o);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) q.a[rb] = pk_rd_a<HALF>(slot, rb, o);
+}
+
+template <int NRB>
+__device__ __forceinline__ void pk_read_scales(ScaleWords<NRB>& s, const uint8_t* slot, const LdsOffs& o)
+{
+#pragma unroll
+    for (int c = 0; c < 2; ++c) s.b[c] = pk_rd_s(slot, o.obs + 32 * pk::SCB * c);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) s.a[rb] = pk_rd_s(slot, o.osa + 32 * pk::SCB * rb);
+}
+
+// One half superstep.  The MFMAs consume the fragments bf, af (converted during the
+// previous half); meanwhile the raw bytes q of the next half (read from LDS during the
+// previous half, so their reads have had a whole half to land) are converted into bf, af,
+// and the raw bytes of the half after that are read from `nxt` (the next superstep's slot)
+// into q.  HALF = 0: the next half is half 1 of this superstep (scales s); the half after
+// is half 0 of the next superstep, whose scale words are read too and replace s once this
+// half's conversions are done.  HALF = 1: the next half is half 0 of the next superstep;
+// the half after is its half 1.
+template <int NRB, int HALF>
+__device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], h8_t (&af)[2][NRB], RawHalf<NRB>& q,
+                                        ScaleWords<NRB>& s, const uint8_t* nxt, const LdsOffs& o, uint32_t tsel)
+{
+    RawHalf<NRB> qn;
+    ScaleWords<NRB> sn;
     if constexpr (HALF == 0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) qb[c] = pk_rd_b<1>(cur, c, o);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) qa[rb] = pk_rd_a<1>(cur, rb, o);
+        pk_read_scales<NRB>(sn, nxt, o);
+        pk_read_raw<NRB, 0>(qn, nxt, o);
     } else {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) srow[c] = pk_rd_s(nxt, o.obs + 32 * SCB * c);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) arow[rb] = pk_rd_s(nxt, o.osa + 32 * SCB * rb);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) qb[c] = pk_rd_b<0>(nxt, c, o);
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) qa[rb] = pk_rd_a<0>(nxt, rb, o);
+        pk_read_raw<NRB, 1>(qn, nxt, o);
     }
     pk_mfmas<NRB>(acc, bf[0], af[0]);
     pk_mfmas<NRB>(acc, bf[1], af[1]);
-    pk_dequant<NRB, 1 - HALF>(bf, af, qb, qa, srow, arow, tsel);
+    pk_dequant<NRB, 1 - HALF>(bf, af, q.b, q.a, s.b, s.a, tsel);
+    q = qn;
+    if constexpr (HALF == 0) s = sn;
 }
 
 // The steady-state load wait of the ring above: AHEAD = slots - 2 supersteps stay in flight.
@@ -633,11 +661,11 @@ __device__ __forceinline__ void pk_wait_steady(int n)
 // One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)), K a
 // multiple of 64 (the last superstep holds k - 256 (supers - 1) K values).  All 8 waves
 // execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs per B
-// fragment; SCL is how the scales are fetched (ScaleMode).  In superstep t, half 0
-// computes and converts half 1 of slot t; then the wave waits for its own loads of
-// superstep t + 1, and the barrier both publishes superstep t + 1 and frees slot t (no
-// wave reads it any more), which is refilled at once with superstep t + slots; half 1
-// computes and converts half 0 of superstep t + 1.
+// fragment; SCL is how the scales are fetched (ScaleMode).  Raw bytes are read from LDS two
+// halves before their MFMAs and converted one half before.  At the start of superstep t the
+// wave waits for its own loads of superstep t + 1, and the barrier both publishes
+// superstep t + 1 (read during superstep t) and frees slot t (already read during
+// superstep t - 1), which is refilled at once with superstep t + slots.
 template <int NRB, int SCL>
 __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_,
                                         uint8_t* smem)
@@ -672,32 +700,24 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
     barrier_lds();
     const uint32_t tsel = 0x0c0c0000u | ((uint32_t)(4 + tq) << 8) | (uint32_t)tq;
     const LdsOffs lo = pk_lds_offsets<NRB>(lane, cw, tq);
-    u2_t srow[2], arow[NRB];
+    // fragments of half 0 of superstep 0, raw bytes of its half 1 and its scale words
     h8_t bf[2][2], af[2][NRB];
+    RawHalf<NRB> q;
+    ScaleWords<NRB> sw;
     {
-        u2_t qb[2], qa[NRB];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            srow[c] = pk_rd_s(ring, lo.obs + 32 * SCB * c);
-            qb[c] = pk_rd_b<0>(ring, c, lo);
-        }
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            arow[rb] = pk_rd_s(ring, lo.osa + 32 * SCB * rb);
-            qa[rb] = pk_rd_a<0>(ring, rb, lo);
-        }
-        pk_dequant<NRB, 0>(bf, af, qb, qa, srow, arow, tsel);
+        RawHalf<NRB> q0;
+        pk_read_scales<NRB>(sw, ring, lo);
+        pk_read_raw<NRB, 0>(q0, ring, lo);
+        pk_read_raw<NRB, 1>(q, ring, lo);
+        pk_dequant<NRB, 0>(bf, af, q0.b, q0.a, sw.b, sw.a, tsel);
     }
 
     const int wait_steady = (nslots - 2) * L.ops;
-    int cs = 0;
+    int cs = 0;   // slot of superstep t
     for (int t = 0; t < supers; ++t) {
-        const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
-        const uint8_t* cur = ring + cs * sbytes;
-        // after the last superstep the "next" reads land on a slot that holds no data any
-        // more: harmless, and their results are unused
-        const uint8_t* nxt = ring + ns * sbytes;
-        pk_half<NRB, 0>(acc, bf, af, srow, arow, cur, nxt, lo, tsel);
+        // superstep t + 1 must have landed (this wave's loads; loads complete in issue
+        // order, so later supersteps stay in flight) before the barrier publishes it; the
+        // barrier also frees slot t, whose bytes are all in registers by now: refill it
         if (t + nslots - 1 < supers) {
             pk_wait_steady<NRB, SCL>(wait_steady);   // supersteps t + 2 .. t + slots - 1 in flight
         } else if (t + 1 < supers) {
@@ -705,7 +725,12 @@ __device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int 
         }
         barrier_lds();
         if (t + nslots < supers) pk_issue<SCL>(ring + cs * sbytes, t + nslots, kt_of(t + nslots), L, lane);
-        pk_half<NRB, 1>(acc, bf, af, srow, arow, cur, nxt, lo, tsel);
+        const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
+        // in the last superstep the reads of the "next" slot land on bytes that are no
+        // superstep's: harmless, and their results are unused
+        const uint8_t* nxt = ring + ns * sbytes;
+        pk_half<NRB, 0>(acc, bf, af, q, sw, nxt, lo, tsel);
+        pk_half<NRB, 1>(acc, bf, af, q, sw, nxt, lo, tsel);
         cs = ns;
     }
     // every ring read has completed and every load has landed before the reduction area
