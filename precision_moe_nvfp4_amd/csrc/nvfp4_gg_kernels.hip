@@ -109,6 +109,9 @@ __host__ __device__ constexpr int ring_slots(int rpad)
 // block and 32-row block, the three element groups handed to the other K quarters (one u4
 // per lane each)
 constexpr int RED_WAVE = 2 * (RMAX / 32) * 3 * 64 * 16;
+// staged output rows of the epilogue (fp16, 128 columns, padded to spread banks)
+constexpr int STAGE_ROW = BN * 2 + 16;
+static_assert(RMAX * STAGE_ROW <= LDS_BYTES, "staged output tile must fit in LDS");
 static_assert(ring_slots(RMAX) >= 3, "the tallest tile needs at least 3 ring slots");
 static_assert(8 * RED_WAVE <= LDS_BYTES, "reduction area must fit in LDS");
 }  // namespace pk
@@ -354,8 +357,13 @@ __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], u
                 o[c][rb][i++] = reinterpret_cast<const u4_t*>(smem + (cw + 2 * p) * RED_WAVE)[((c * NRB + rb) * 3 + slot) * 64 + lane];
             }
     const int j = lane & 31, h = lane >> 5;
-    // the whole tile is in bounds with 8-byte aligned rows: one uniform test
+    // all 128 columns in bounds and 16-byte aligned rows (one uniform test): the reduced fp16
+    // tile is staged in LDS as rows and leaves in whole 128-byte lines, 16 bytes per lane,
+    // with the non-temporal hint (C is written once and not read again here); otherwise
+    // each lane stores its own 4 columns (8 bytes, or element-wise at the edge)
+    const bool staged = (ldc & 7) == 0 && col + BN <= n;
     const bool full = (ldc & 3) == 0 && col + BN <= n;
+    if (staged) barrier_lds();   // the staged rows overwrite the exchange area: all reads done
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -369,11 +377,17 @@ __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], u
                        __uint_as_float(o[c][rb][2][e]);
             }
             const int r = rb * 32 + j;
-            if (r >= rows) continue;
             const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
             const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
+            const int tc = 64 * cw + 32 * c + 8 * T + 4 * h;   // column inside the tile
+            if (staged) {
+                *reinterpret_cast<u2_t*>(smem + r * STAGE_ROW + 2 * tc) =
+                    u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
+                continue;
+            }
+            if (r >= rows) continue;
             uint16_t* crow = c0 + (long)r * ldc;
-            const int cc = col + 64 * cw + 32 * c + 8 * T + 4 * h;
+            const int cc = col + tc;
             if (full) {
                 *reinterpret_cast<u2_t*>(crow + cc) =
                     u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
@@ -384,6 +398,15 @@ __device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], u
                 if (cc + 3 < n) crow[cc + 3] = h3;
             }
         }
+    if (staged) {
+        barrier_lds();
+        // 16 lanes per 256-byte tile row, 32 rows per pass of the 512 threads
+        const int tid = threadIdx.x, chunk = tid & 15;
+        for (int r = tid >> 4; r < rows; r += THREADS / 16) {
+            const u4_t val = *reinterpret_cast<const u4_t*>(smem + r * STAGE_ROW + 16 * chunk);
+            __builtin_nontemporal_store(val, reinterpret_cast<u4_t*>(c0 + (long)r * ldc + col + 8 * chunk));
+        }
+    }
 }
 
 template <int NRB>
