@@ -10,7 +10,9 @@ Timing protocol (per shape):
   * K calls are captured into one HIP graph (torch.cuda.CUDAGraph) and replayed after W
     warm-up calls; HIP events on the replay stream bracket the replay; avg per call = t/K;
   * a second figure re-runs the same K calls as plain launches (host launch overhead
-    included), and a third uses one input set only ("warm").
+    included), and a third uses one input set only ("warm");
+  * "us_per_call_spread" gives min / median / max over the headline replay and 4 further
+    replays of the same cold graph.
 The roofline object prices the kernel against the fp16 MFMA dense peak (the path's
 contraction runs on v_mfma_f32_32x32x16_f16) with the algorithmic flops per launch.
 
@@ -37,6 +39,7 @@ PAGE_US = {"c1": 10.5, "c2": 14.3, "c3": 45.0, "c4": 47.5}   # B200 timings prin
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
 COLD_BYTES = 1 << 30
+SPREAD_REPLAYS = 4             # further timed replays of the cold graph, for min/median/max
 KERNEL_SOURCE = os.path.join(ROOT, "precision_moe_nvfp4_amd", "csrc", "nvfp4_gg_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_gg_c1.md")
 
@@ -141,20 +144,25 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
         launches([i % R for i in range(warmup)])
     torch.cuda.synchronize()
 
-    def graph_time(seq):
+    def graph_time(seq, extra=0):
+        """Average per call of one timed replay of the captured sequence; with extra > 0 also
+        the per-call averages of that many further replays (run-to-run spread)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             launches(seq)
         with torch.cuda.stream(stream):
             g.replay()   # warm replay
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1000.0 / len(seq)
+        times = []
+        for _ in range(1 + extra):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1000.0 / len(seq))
+        return times if extra else times[0]
 
     def direct_time(seq):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -166,7 +174,9 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1000.0 / len(seq)
 
-    us_cold = graph_time(cold_seq)
+    cold = graph_time(cold_seq, extra=SPREAD_REPLAYS)
+    us_cold = cold[0]   # the headline: exactly one timed replay of the K calls
+    spread = sorted(cold)
     us_direct = None if cold_only else direct_time(cold_seq)
     us_warm = None if cold_only else graph_time(warm_seq)
     t_roof_us = max(nbytes / (PEAK_HBM_GBS * 1e3), flops / (PEAK_F16_TFLOPS * 1e6))
@@ -174,6 +184,8 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
         "us_per_call": round(us_cold, 3),
         "us_per_call_direct_launch": None if us_direct is None else round(us_direct, 3),
         "us_per_call_warm": None if us_warm is None else round(us_warm, 3),
+        "us_per_call_spread": {"min": round(spread[0], 3), "median": round(spread[len(spread) // 2], 3),
+                               "max": round(spread[-1], 3), "replays": len(spread)},
         "eff_tflops": round(flops / us_cold / 1e6, 1),
         "eff_hbm_tbs": round(nbytes / us_cold / 1e6, 3),
         "algorithmic_bytes": nbytes,
