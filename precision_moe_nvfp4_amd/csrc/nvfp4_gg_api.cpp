@@ -65,13 +65,15 @@ int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Estimated cycles of one tile on one CU, per compute step of 64 K (measured on MI355X):
+// Estimated cycles of one tile on one CU, per compute step of 64 K (fitted on MI355X):
 //   * MFMA: per SIMD 4 * rpad/32 MFMAs 32x32x16 f16 at ~35 cycles;
 //   * VALU: per SIMD ~2 x 26 instructions for B plus 18 per 64 tile rows for A, at ~4.6
-//     cycles (the conversions are not full rate); it overlaps the MFMAs;
+//     cycles (the conversions are not full rate);
 //   * operand bytes: (128 + rows) rows x 36 B arrive at ~21 B per cycle per CU from L2.
 // The slowest of the three sets the step; the first superstep's loads and the epilogue
-// are not overlapped.
+// are not overlapped.  The model only has to rank the candidate chunk heights: timing every
+// height on the box picks the same one as the model on each of the page shapes and on the
+// dense 8192x4096x4096 shape (absolute times are ~2.5x the model's).
 double tile_cycles(int rows, int k)
 {
     const int rpad = (rows + 31) & ~31;
