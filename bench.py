@@ -42,6 +42,7 @@ COLD_BYTES = 1 << 30
 SPREAD_REPLAYS = 4             # further timed replays of the cold graph, for min/median/max
 KERNEL_SOURCE = os.path.join(ROOT, "precision_moe_nvfp4_amd", "csrc", "nvfp4_gg_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_gg_c1.md")
+SHAPES_PROFILE = os.path.join(ROOT, "profiles", "kernel_traffic_mfma_nvfp4_gg_c2_c3_c4.md")
 
 
 DENSE = "8192:4096:4096"
@@ -73,6 +74,22 @@ def recorded_traffic():
     if not h or not t or h.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
+
+
+def recorded_shape_traffic():
+    """HBM bytes per launch (read + write, counter-scaled) per page shape from the committed
+    rocprofv3 summaries, if they were taken on the current kernel source; {} otherwise."""
+    out = {}
+    t = recorded_traffic()
+    if t is not None:
+        out[HEADLINE] = t
+    if os.path.exists(SHAPES_PROFILE):
+        text = open(SHAPES_PROFILE).read()
+        h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+        if h and h.group(1) == kernel_source_hash():
+            for m in re.finditer(r"^\| (c\d) \|[^|]*\|[^|]*\| ([0-9,]+) \| ([0-9,]+) \|", text, re.M):
+                out[m.group(1)] = float(m.group(2).replace(",", "")) + float(m.group(3).replace(",", ""))
+    return out
 
 
 def shape_of(name):
@@ -282,6 +299,11 @@ def main():
         shapes[nm] = time_shape(torch, gg, HEADLINE, a.steps, a.warmup, dev, cold_only=True, blocked=True)
         shapes[nm]["page_b200_us"] = None
         print(f"bench: {nm} -> {shapes[nm]}", file=sys.stderr, flush=True)
+    traffic = recorded_shape_traffic()
+    for nm, res in shapes.items():
+        tb = traffic.get(nm)
+        res["counter_traffic_bytes"] = tb
+        res["counter_hbm_tbs"] = None if tb is None else round(tb / res["us_per_call"] / 1e6, 3)
     head = shapes[HEADLINE]
     cfg = CONFIGS[HEADLINE]
     us = head["us_per_call"]
