@@ -240,7 +240,20 @@ def cpu_baseline(name):
     us = times[len(times) // 2] * 1e6
     return {"value": round(us, 1), "unit": "us", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{len(times)} full {name} grouped calls (g={cfg.g}, n={cfg.n}, k={cfg.k}) in "
-                      f"{time.perf_counter() - t_start:.1f} s, median; packed inputs to fp16 C, decode included"}
+                      f"{time.perf_counter() - t_start:.1f} s, median; packed inputs to fp16 C, decode included; "
+                      f"host CPU: {host_cpu_model()}"}
+
+
+def host_cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def calibrate_copy(torch):
