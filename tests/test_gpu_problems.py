@@ -21,7 +21,9 @@ CASES = [
 ]
 
 
-def run_problems(problems, layout):
+def run_problems(problems, layout, repeats=1, expect=None):
+    """Plan once, run `repeats` times (C canary-filled before each run) and check every run
+    against the oracle; `expect(info)` may assert properties of the plan first."""
     dev = torch.device("cuda", 0)
     inps = [make_inputs([m], n, k, seed=1000 + 7 * i + m) for i, (m, n, k, _) in enumerate(problems)]
     conv = (lambda s, k: oracle.scales_to_blocked(s, k, pad=0x7F)) if layout == gg.SCALES_BLOCKED else \
@@ -37,8 +39,24 @@ def run_problems(problems, layout):
         bufs.append(buf)
         views.append(buf[PAD:PAD + m * ld])
     plan = gg.nvfp4_gg_plan_problems(problems, scale_layout=layout)
-    gg.nvfp4_gg_run(plan, A, B, SFA, SFB, views)
-    torch.cuda.synchronize()
+    if expect is not None:
+        expect(gg.nvfp4_gg_plan_info(plan))
+    first = None
+    for rep in range(repeats):
+        for buf in bufs:
+            buf.fill_(CANARY)
+        gg.nvfp4_gg_run(plan, A, B, SFA, SFB, views)
+        torch.cuda.synchronize()
+        if first is None:
+            check_outputs(problems, bufs, inps, f"run {rep}")
+            first = [buf.cpu().numpy().copy() for buf in bufs]
+        else:
+            # later runs of the same plan: bit-identical to the first (a fixed summation order)
+            for i, buf in enumerate(bufs):
+                assert np.array_equal(buf.cpu().numpy(), first[i]), f"run {rep}: group {i} differs from run 0"
+
+
+def check_outputs(problems, bufs, inps, what):
     for i, ((m, n, k, ldc), buf, inp) in enumerate(zip(problems, bufs, inps)):
         ld = ldc or n
         h = buf.cpu().numpy().view(np.uint16)
@@ -46,7 +64,7 @@ def run_problems(problems, layout):
         c = h[PAD:PAD + m * ld].reshape(m, ld)
         assert np.all(c[:, n:] == CANARY), f"group {i}: write beyond column n"
         if m:
-            check(inp, [np.ascontiguousarray(c[:, :n])], f"group {i} (m={m} n={n} k={k} ldc={ldc})")
+            check(inp, [np.ascontiguousarray(c[:, :n])], f"{what}: group {i} (m={m} n={n} k={k} ldc={ldc})")
 
 
 @pytest.mark.parametrize("layout", [gg.SCALES_ROW_MAJOR, gg.SCALES_BLOCKED])
