@@ -4,9 +4,10 @@ A tile of 32, 64 or 96 rows streams K through a ring of 7, 5 or 5 superstep slot
 each): the first slots are filled up front, and from then on the slot just consumed is
 refilled at the start of every superstep, with a constant load wait in the steady state and a
 shrinking one in the last supersteps.  These cases put the number of supersteps below, at and
-beyond the slot count (several wraps), with and without a short last superstep, for each tile
-height and both scale layouts (whose load counts per superstep differ), and check every
-element against the oracle (same bar and canaries as the per-group tests).  The planner's
+beyond the slot count (several wraps, up to 256 supersteps), with and without a short last
+superstep, for each tile height and both scale layouts (whose load counts per superstep
+differ), plus a very wide n (many tiles per workgroup), and check every element against the
+oracle (same bar and canaries as the per-group tests).  The planner's
 chosen tile height is asserted, so that each case runs the ring it is meant to.
 """
 import pytest
@@ -27,6 +28,11 @@ CASES = [
     ([(90, 4096, 1344, 0)] * 8, 96),
     # 90-row tiles: 4, 5 and 11 supersteps
     ([(90, 4096, 1024, 0)] * 4 + [(90, 4096, 1280, 0)] * 2 + [(90, 4096, 2816, 0)] * 2, 96),
+    # long K: 256 supersteps (36 wraps of a 7-slot ring) and the largest load offsets
+    ([(3, 130, 65536, 0), (3, 64, 65536 - 192, 0)], 96),
+    # wide n: 1024 column tiles over 256 workgroups (4 tiles each), one and 33 rows
+    ([(1, 131072, 256, 0)], 96),
+    ([(33, 131072, 512, 0)], 96),
 ]
 
 
