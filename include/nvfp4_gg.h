@@ -11,7 +11,8 @@
  * packed FP4 E2M1 codes, sfa[m, k/16] and sfb[n, k/16] of FP8 E4M3 scales, c[m, n] fp16,
  * one (m, n, k) problem per group), its kernel configuration block the data types
  * (Float4E2M1FN, Float8E4M3FN, 16 elements per scale, Float16 output, Float32
- * accumulator) and the comment before its launch the product "C = A * SFA * B * SFB".
+ * accumulator), and the comment before its kernel launch states that each operand is
+ * multiplied by its own scale factors before the product is formed.
  * Output rounding is round-to-nearest-even, as in the epilogue_store function of the page
  * "kernelindex submission 498317".
  *
@@ -23,11 +24,12 @@
  *   C_i   [m_i][n] fp16 (IEEE binary16).
  * n and k are the same for every group; m_i varies (m_i = 0 is allowed and writes nothing).
  *
- * Ownership: the caller owns every device buffer it passes.  A plan owns host memory and
- * one small device buffer on its device (its tile schedule: 16 bytes per tile and 4 bytes
- * per workgroup), allocated by nvfp4_gg_plan and freed by nvfp4_gg_destroy.
+ * Ownership: the caller owns every device buffer it passes.  A plan owns host memory only:
+ * its schedule travels in the kernel arguments of every call, so nvfp4_gg_plan allocates
+ * nothing on a device and nvfp4_gg_destroy performs no device work (no synchronisation).
  * Asynchrony: nvfp4_gg_run only enqueues work on the given stream; it never synchronises,
- * allocates device memory, prints or throws.
+ * allocates memory, prints or throws.  A call captured into a HIP graph carries everything
+ * it needs in its kernel node, so the graph stays valid after the plan is destroyed.
  * Threading: a plan is immutable after nvfp4_gg_plan returns; several threads may call
  * nvfp4_gg_run on one plan concurrently.  Distinct plans are independent.
  * Errors: every entry point returns a status code; nothing is thrown across this ABI.
@@ -100,38 +102,47 @@ typedef struct {
     int m, n, k, ldc;
 } nvfp4_gg_problem_t;
 
-/* What a plan decided; filled by nvfp4_gg_plan_info. */
+/* What a plan decided; filled by nvfp4_gg_plan_info.  A work unit is up to unit_rows[p]
+ * rows of the group at schedule position p times unit_cols[p] columns, over its whole K. */
 typedef struct {
     int g, n, k;           /* n and k shared by every group, or 0 where they differ */
     int device;            /* HIP device ordinal, or NVFP4_GG_DEVICE_NONE */
     int num_cus;           /* compute units the schedule was sized for */
-    int tile_m, tile_n;    /* largest output tile of one workgroup (rows, columns) */
-    int total_tiles;       /* tiles over all groups */
+    int tile_m, tile_n;    /* largest unit of the plan (rows, columns) */
+    int total_tiles;       /* work units over all groups */
     int grid;              /* workgroups launched per call */
     int block;             /* threads per workgroup */
     int lds_bytes;         /* LDS per workgroup */
-    int variant;           /* kernel variant id (see the design notes) */
+    int variant;           /* kernel variant id: 5 row-major scales, 6 blocked scales */
     int order[NVFP4_GG_MAX_GROUPS];       /* group processed at schedule position p */
-    int tile_begin[NVFP4_GG_MAX_GROUPS + 1]; /* exclusive tile prefix in schedule order */
+    int tile_begin[NVFP4_GG_MAX_GROUPS + 1]; /* exclusive unit prefix in schedule order */
     int scale_layout;      /* nvfp4_gg_scale_layout_t the plan's runs read */
+    int unit_rows[NVFP4_GG_MAX_GROUPS];   /* unit height at schedule position p (0: m = 0) */
+    int unit_cols[NVFP4_GG_MAX_GROUPS];   /* unit width at schedule position p */
+    double est_us;         /* the planner's cost-model estimate of one call (microseconds) */
 } nvfp4_gg_plan_info_t;
 
 /*
  * Build a plan for g groups with row counts m[0..g-1] (host array, copied), and shared
- * n and k: validation, the largest-work-first group order and its tile prefix sum (the
- * host planning of custom_kernel on the page "kernelindex submission 503584": groups
- * sorted by tile work, prefix of per-group tile counts), the tile height, and a balanced
- * schedule of the tiles over the device's workgroups, which is uploaded once to device
- * memory owned by the plan (synchronous hipMalloc + hipMemcpy; allocation failure:
- * NVFP4_GG_ENOMEM).  Plans are meant to be built once per shape and reused.
+ * n and k: validation, the largest-work-first group order and its per-group unit counts
+ * and prefix sum (the host planning of custom_kernel on the page "kernelindex submission
+ * 503584": groups sorted by tile work, prefix of per-group tile counts), and each group's
+ * unit shape, chosen by a cost model so that the persistent grid's contiguous shares of
+ * the unit sequence take about the same time.  Host work only: nothing is allocated on
+ * or copied to a device.  Plans are meant to be built once per shape and reused.
  *   device: HIP device ordinal, -1 for the current device, or NVFP4_GG_DEVICE_NONE (host
- *   only: nothing is allocated on a device).
+ *   only: the HIP runtime is not touched).
  * Requirements: 1 <= g <= NVFP4_GG_MAX_GROUPS, 1 <= n <= 2^20, 64 <= k <= 2^20 and
  * k % 64 == 0, 0 <= m_i <= 2^20; else NVFP4_GG_EINVAL (g above the maximum:
  * NVFP4_GG_EUNSUPPORTED).  (The group_gemm host function of "kernelindex submission
  * 498317" requires k % 256 == 0; here K values beyond the last multiple of 256 are handled
- * by a shorter last K step, so every multiple of 64 is accepted.)  A device that is not gfx950: NVFP4_GG_EUNSUPPORTED.
+ * by a shorter last K step, so every multiple of 64 is accepted.)  A device that is not
+ * gfx950: NVFP4_GG_EUNSUPPORTED.  Host allocation failure: NVFP4_GG_ENOMEM.
  * On success *out holds a new plan, released with nvfp4_gg_destroy; on failure *out = NULL.
+ * Diagnostics: if the environment variable NVFP4_GG_FORCE_SHAPE holds "na,nb" naming a
+ * compiled unit shape (32 na rows x 32 nb columns), every group of the plan uses it instead
+ * of the planner's choice (for tests and measurements; results are the same, only the
+ * schedule differs).
  */
 nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k,
                                 int device);
@@ -193,9 +204,8 @@ nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan,
 /* Copy the plan's decisions into *info.  NVFP4_GG_EINVAL on a null argument. */
 nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_plan_info_t* info);
 
-/* Release a plan (NULL is ignored).  Waits until the plan's device has finished its
- * outstanding work (an enqueued call may still read the plan's schedule), then frees the
- * plan's device and host memory. */
+/* Release a plan's host memory (NULL is ignored).  No device work and no synchronisation:
+ * calls already enqueued with the plan, and graphs that captured them, do not read it. */
 void nvfp4_gg_destroy(nvfp4_gg_plan_t plan);
 
 /* Static English text for a status code; never NULL. */

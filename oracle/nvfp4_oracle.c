@@ -11,10 +11,11 @@
  *
  * for every group i, row r < m_i and column c < n, where a, b are FP4 E2M1
  * values and sa, sb are FP8 E4M3FN scale values, one per 16 consecutive K.
- *   - "C = A * SFA * B * SFB" and the operand shapes a[m, k/2], b[n, k/2],
- *     sfa[m, k/16], sfb[n, k/16], c[m, n] fp16 are from the custom_kernel
- *     docstring and the closing comment of the kernel launch on the page
- *     "kernelindex submission 503584"; the data types (Float4E2M1FN data,
+ *   - Each operand scaled by its own scale factors, then multiplied (the
+ *     comment before the kernel launch), and the operand shapes a[m, k/2],
+ *     b[n, k/2], sfa[m, k/16], sfb[n, k/16], c[m, n] fp16 (the custom_kernel
+ *     docstring) are from the page "kernelindex submission 503584"; the data
+ *     types (Float4E2M1FN data,
  *     Float8E4M3FN scales, 16 elements per scale, Float16 output) are that
  *     page's kernel configuration block.
  *   - The products are summed in fp64.  Every product is an integer multiple of

@@ -53,6 +53,9 @@ class PlanInfo(ctypes.Structure):
         ("order", ctypes.c_int * MAX_GROUPS),
         ("tile_begin", ctypes.c_int * (MAX_GROUPS + 1)),
         ("scale_layout", ctypes.c_int),
+        ("unit_rows", ctypes.c_int * MAX_GROUPS),
+        ("unit_cols", ctypes.c_int * MAX_GROUPS),
+        ("est_us", ctypes.c_double),
     ]
 
 

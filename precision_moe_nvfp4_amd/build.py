@@ -21,9 +21,6 @@ FLAGS = [
     "--offload-arch=gfx950", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in ordinary VGPRs (avoids AGPR<->VGPR copies of the
-    # loop-carried accumulators)
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -1,22 +1,28 @@
 // Host side of the NVFP4 grouped GEMM C ABI: validation, planning and launch.
 //
 // Planning follows the host path of custom_kernel on the page "kernelindex submission
-// 503584" in spirit (groups ordered by work, tiles enumerated over per-group tile counts),
-// but the tile list is built here once per shape and balanced across the compute units:
-//   * every group's rows are cut into equal chunks of at most R rows (multiples of 32) and
-//     the columns into 128-wide tiles, for each candidate R in {32, 64, 96};
-//   * a cost model (MFMA cycles plus the dequantisation VALU cycles that the tile height
-//     implies, per SIMD) prices each tile;
-//   * tiles that read the same B columns (same group, same column tile) are kept on one
-//     XCD, XCDs are balanced, and inside an XCD tiles are dealt largest first to the least
-//     loaded workgroup (LPT);
-//   * the candidate R with the smallest estimated makespan wins.
-// The group table travels by value in the kernel arguments on every call; the tile list
-// is uploaded to device memory once, when the plan is built.
+// 503584" in spirit (groups ordered by work, per-group tile counts and their prefix sum
+// drive a persistent grid), with work units sized for gfx950:
+//   * a unit is up to 32 NA rows of one group times 32 NB columns over the whole K; the
+//     four waves of a workgroup split every K superstep and each holds the unit's NA x NB
+//     accumulator blocks (at most 20), and the shapes the kernel is compiled for are
+//     listed in nvfp4_gg_internal.h;
+//   * a cost model (MFMA cycles, the conversion VALU that shares the MFMA's issue slots,
+//     operand bytes, fixed prologue and epilogue cycles) prices a unit of each shape;
+//   * each group gets one shape; starting from every group's most efficient shape, a
+//     coordinate descent over the groups' shapes minimises the estimated makespan of the
+//     kernel's own partition (workgroup v runs units [U v / V, U (v+1) / V) of the unit
+//     sequence);
+//   * the plan is the group table alone: it travels in the kernel arguments of every call,
+//     so a plan holds host memory only and a call touches no device memory besides the
+//     operands.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -33,21 +39,16 @@ struct nvfp4_gg_plan_s {
     int n, k;                    // shared by every group, or 0 where the groups differ
     int device;
     int num_cus;
-    int variant;
     int scale_layout;            // nvfp4_gg_scale_layout_t
-    VariantShape shape;
-    int chunk_rows;              // chosen maximum rows per tile
-    int total_tiles;
-    int grid;
-    double est_cycles;           // estimated makespan of the tile schedule
+    int units;                   // units over all groups
+    int vq;                      // virtual workgroups per XCD
+    int grid;                    // 8 vq, or 0 when there is no work
+    double est_cycles;           // estimated makespan (cycles of one CU)
     std::vector<int> m;          // caller order
     std::vector<int> ns, ks, ldcs;  // caller order
     std::vector<int> order;      // order[p] = caller group at schedule position p
-    std::vector<int> tile_begin; // per-group tile prefix in schedule order (informational)
-    std::vector<TileDesc> tiles; // tiles grouped by workgroup (group = schedule position)
-    std::vector<int> wg_begin;   // size grid + 1
-    TileDesc* d_tiles = nullptr;
-    int* d_wg_begin = nullptr;
+    std::vector<int> na, nb;     // unit shape per schedule position (0 for m = 0)
+    std::vector<int> unit_begin; // per-group unit prefix in schedule order (size g + 1)
 };
 
 namespace {
@@ -56,100 +57,210 @@ constexpr uint32_t kPlanMagic = 0x4E564634u;  // "NVF4"
 constexpr int kMaxRows = 1 << 20;
 constexpr int kNominalCUs = 256;               // MI355X
 constexpr int kXcds = 8;                       // workgroup b runs on XCD b % 8
-constexpr int kTileCols = 128;
-constexpr int kStepK = 64;
+
+struct Shape {
+    int na, nb;
+};
+const Shape kShapes[] = {
+#define NVFP4GG_SHAPE(NA_, NB_) Shape{NA_, NB_},
+    NVFP4GG_UNIT_SHAPES(NVFP4GG_SHAPE)
+#undef NVFP4GG_SHAPE
+};
 
 bool plan_ok(const nvfp4_gg_plan_s* p) { return p != nullptr && p->magic == kPlanMagic; }
 
-int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Estimated cycles of one tile on one CU, per compute step of 64 K (fitted on MI355X):
-//   * MFMA: per SIMD 4 * rpad/32 MFMAs 32x32x16 f16 at ~35 cycles;
-//   * VALU: per SIMD ~2 x 26 instructions for B plus 18 per 64 tile rows for A, at ~4.6
-//     cycles (the conversions are not full rate);
-//   * operand bytes: (128 + rows) rows x 36 B arrive at ~21 B per cycle per CU from L2.
-// The slowest of the three sets the step; the first superstep's loads and the epilogue
-// are not overlapped.  The model only has to rank the candidate chunk heights: timing every
-// height on the box picks the same one as the model on each of the page shapes and on the
-// dense 8192x4096x4096 shape (absolute times are ~2.5x the model's).
-double tile_cycles(int rows, int k)
+// Estimated cycles of one unit of shape (na, nb) with K = k on one CU, fitted to the
+// kernel's own per-phase cycle counts on MI355X:
+//   * the main loop issues, per superstep and wave, 4 na nb MFMAs 32x32x16 f16 and
+//     ~33 (na + nb) conversion instructions (four FP4 conversions and four packed multiplies
+//     per fragment and step); an MFMA holds the issue port ~19 of its 32 cycles, so the
+//     conversions only partly hide behind it: ~110 na nb + 172 (na + nb) cycles per
+//     superstep, barrier and LDS reads included;
+//   * plus the pipeline fill (the first superstep's operands from HBM) and the epilogue
+//     (the four K-quarter partial tiles added through LDS, fp16 rounding, stores).
+double unit_cycles(int na, int nb, int k)
 {
-    const int rpad = (rows + 31) & ~31;
-    const int steps = (k + 255) / 256 * (256 / kStepK);   // a short last superstep costs a full one
-    const double mfma = 4.0 * (rpad / 32) * 35.0;
-    const double valu = (2.0 * 26.0 + 18.0 * ((rpad + 63) / 64)) * 4.6;
-    const double load = (kTileCols + rpad) * 36.0 / 21.0;
-    return steps * std::max(std::max(mfma, valu), load) + 4.0 * load + 3000.0;
+    const double nm = (double)na * nb;
+    const double super = 110.0 * nm + 172.0 * (na + nb);
+    const double nsup = (double)ceil_div(k, 256);
+    return nsup * super + 8300.0 + 535.0 * nm;
 }
 
-struct Schedule {
-    int chunk_rows = 0;
-    double makespan = 0;
-    std::vector<std::vector<TileDesc>> per_wg;
+struct GroupDims {
+    int m, n, k;
 };
 
-// Build and balance the tile list for chunk height R (group indices are schedule positions;
-// group gi has m_sched[gi] rows, n_sched[gi] columns and K = k_sched[gi]).
-Schedule build_schedule(int R, const std::vector<int>& m_sched, const std::vector<int>& n_sched,
-                        const std::vector<int>& k_sched, int num_wgs)
+long group_units(const GroupDims& d, const Shape& s)
 {
-    Schedule S;
-    S.chunk_rows = R;
-    S.per_wg.assign(num_wgs, {});
-    struct Cls {
-        double cost;
-        std::vector<std::pair<double, TileDesc>> tiles;
-    };
-    std::vector<Cls> classes;
-    for (int gi = 0; gi < (int)m_sched.size(); ++gi) {
-        const int mi = m_sched[gi], k = k_sched[gi];
-        if (mi <= 0) continue;
-        const int ntiles_n = ceil_div(n_sched[gi], kTileCols);
-        const int chunks = ceil_div(mi, R);
-        const int rp = (ceil_div(mi, chunks) + 31) / 32 * 32;
-        for (int tn = 0; tn < ntiles_n; ++tn) {
-            Cls c{0.0, {}};
-            for (int row0 = 0; row0 < mi; row0 += rp) {
-                const int rows = std::min(rp, mi - row0);
-                const double cost = tile_cycles(rows, k);
-                c.tiles.push_back({cost, TileDesc{gi, row0, rows, tn * kTileCols}});
-                c.cost += cost;
+    if (d.m == 0) return 0;
+    return ceil_div(d.m, 32L * s.na) * ceil_div(d.n, 32L * s.nb);
+}
+
+// Makespan of the kernel's partition: the unit sequence (groups in schedule order, each
+// group's units of equal cost) dealt in contiguous ranges of equal count to V workgroups.
+double makespan(const std::vector<GroupDims>& dims, const std::vector<int>& shape, int num_cus, long* units_out,
+                int* vq_out)
+{
+    long U = 0;
+    std::vector<long> cnt(dims.size());
+    std::vector<double> cost(dims.size());
+    for (size_t i = 0; i < dims.size(); ++i) {
+        cnt[i] = shape[i] < 0 ? 0 : group_units(dims[i], kShapes[shape[i]]);
+        cost[i] = shape[i] < 0 ? 0.0 : unit_cycles(kShapes[shape[i]].na, kShapes[shape[i]].nb, dims[i].k);
+        U += cnt[i];
+    }
+    if (units_out) *units_out = U;
+    if (U == 0) {
+        if (vq_out) *vq_out = 0;
+        return 0.0;
+    }
+    const int vq = (int)ceil_div(std::min<long>(U, num_cus), kXcds);
+    if (vq_out) *vq_out = vq;
+    const long V = (long)kXcds * vq;
+    // walk the ranges: range v is [U v / V, U (v+1) / V)
+    double worst = 0.0;
+    size_t gi = 0;
+    long gbase = 0;
+    for (long v = 0; v < V; ++v) {
+        const long u0 = U * v / V, u1 = U * (v + 1) / V;
+        double sum = 0.0;
+        long u = u0;
+        while (u < u1) {
+            while (gi + 1 < dims.size() && u >= gbase + cnt[gi]) {
+                gbase += cnt[gi];
+                ++gi;
             }
-            classes.push_back(std::move(c));
+            const long take = std::min(u1, gbase + cnt[gi]) - u;
+            sum += take * cost[gi];
+            u += take;
+        }
+        worst = std::max(worst, sum);
+    }
+    return worst;
+}
+
+// Candidate shapes of one group: the supported shapes, skipping a shape when a shape
+// with fewer row blocks gives the same row chunk count and the same column blocks (it
+// would only add padding rows).
+std::vector<int> candidates(const GroupDims& d)
+{
+    std::vector<int> out;
+    if (d.m == 0) return out;
+    const int nshapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
+    for (int s = 0; s < nshapes; ++s) {
+        const Shape& sh = kShapes[s];
+        const long rch = ceil_div(d.m, 32L * sh.na);
+        bool dominated = false;
+        for (int t = 0; t < nshapes; ++t)
+            if (kShapes[t].nb == sh.nb && kShapes[t].na < sh.na && ceil_div(d.m, 32L * kShapes[t].na) == rch)
+                dominated = true;
+        if (!dominated) out.push_back(s);
+    }
+    return out;
+}
+
+// Shapes for every group (schedule order) with at most `cap` accumulator blocks per unit:
+// start from each group's cheapest shape per useful multiply-accumulate, then coordinate
+// descent on the estimated makespan (ties: smaller total cost) until no single group's
+// change helps.
+std::vector<int> choose_shapes_capped(const std::vector<GroupDims>& dims, int num_cus, int cap, double* est)
+{
+    const size_t g = dims.size();
+    std::vector<std::vector<int>> cand(g);
+    std::vector<int> shape(g, -1);
+    for (size_t i = 0; i < g; ++i) {
+        for (int s : candidates(dims[i]))
+            if (kShapes[s].na * kShapes[s].nb <= cap) cand[i].push_back(s);
+        double best = 0.0;
+        for (int s : cand[i]) {
+            const Shape& sh = kShapes[s];
+            const double work = (double)dims[i].m * dims[i].n;   // useful per unit of K
+            const double eff = work / (group_units(dims[i], sh) * unit_cycles(sh.na, sh.nb, dims[i].k));
+            if (shape[i] < 0 || eff > best) {
+                best = eff;
+                shape[i] = s;
+            }
+        }
+        if (dims[i].m > 0 && shape[i] < 0) {   // no shape within the cap
+            if (est) *est = 1e300;
+            return shape;
         }
     }
-    // classes (tiles sharing B columns) to XCDs, largest first, least-loaded XCD
-    const int xcds = std::min(kXcds, num_wgs);
-    std::vector<int> order(classes.size());
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return classes[a].cost > classes[b].cost; });
-    std::vector<double> xload(xcds, 0.0);
-    std::vector<std::vector<std::pair<double, TileDesc>>> xtiles(xcds);
-    for (int ci : order) {
-        const int x = (int)(std::min_element(xload.begin(), xload.end()) - xload.begin());
-        xload[x] += classes[ci].cost;
-        for (auto& t : classes[ci].tiles) xtiles[x].push_back(t);
+    const auto total = [&](const std::vector<int>& sh) {
+        double t = 0.0;
+        for (size_t i = 0; i < g; ++i)
+            if (sh[i] >= 0) t += group_units(dims[i], kShapes[sh[i]]) * unit_cycles(kShapes[sh[i]].na, kShapes[sh[i]].nb, dims[i].k);
+        return t;
+    };
+    double cur = makespan(dims, shape, num_cus, nullptr, nullptr);
+    double cur_total = total(shape);
+    for (int pass = 0; pass < 8; ++pass) {
+        bool improved = false;
+        for (size_t i = 0; i < g; ++i) {
+            for (int s : cand[i]) {
+                if (s == shape[i]) continue;
+                std::vector<int> trial = shape;
+                trial[i] = s;
+                const double ms = makespan(dims, trial, num_cus, nullptr, nullptr);
+                const double tt = total(trial);
+                if (ms < cur * 0.999 || (ms <= cur * 1.001 && tt < cur_total * 0.999)) {
+                    shape = trial;
+                    cur = ms;
+                    cur_total = tt;
+                    improved = true;
+                }
+            }
+        }
+        if (!improved) break;
     }
-    // inside an XCD: LPT over its workgroups (b = x + xcds * slot); stable order keeps the
-    // tiles of one class next to each other, so they tend to run in the same round
-    std::vector<double> wload(num_wgs, 0.0);
-    for (int x = 0; x < xcds; ++x) {
-        auto& v = xtiles[x];
-        std::stable_sort(v.begin(), v.end(), [](const auto& a, const auto& b) { return a.first > b.first; });
-        std::vector<int> wgs;
-        for (int b = x; b < num_wgs; b += xcds) wgs.push_back(b);
-        for (auto& t : v) {
-            int best = wgs[0];
-            for (int b : wgs)
-                if (wload[b] < wload[best]) best = b;
-            wload[best] += t.first;
-            S.per_wg[best].push_back(t.second);
+    if (est) *est = cur;
+    return shape;
+}
+
+// The shape that NVFP4_GG_FORCE_SHAPE="na,nb" names, if it is a compiled shape; else -1.
+int forced_shape()
+{
+    const char* e = std::getenv("NVFP4_GG_FORCE_SHAPE");
+    int na = 0, nb = 0;
+    if (e == nullptr || std::sscanf(e, "%d,%d", &na, &nb) != 2) return -1;
+    const int nshapes = (int)(sizeof(kShapes) / sizeof(kShapes[0]));
+    for (int s = 0; s < nshapes; ++s)
+        if (kShapes[s].na == na && kShapes[s].nb == nb) return s;
+    return -1;
+}
+
+// The best of the capped searches over every cap a compiled shape has (or the forced shape
+// for every group).
+std::vector<int> choose_shapes(const std::vector<GroupDims>& dims, int num_cus, double* est)
+{
+    const int forced = forced_shape();
+    if (forced >= 0) {
+        std::vector<int> sh(dims.size(), -1);
+        for (size_t i = 0; i < dims.size(); ++i)
+            if (dims[i].m > 0) sh[i] = forced;
+        if (est) *est = makespan(dims, sh, num_cus, nullptr, nullptr);
+        return sh;
+    }
+    std::vector<int> caps;
+    for (const Shape& sh : kShapes) caps.push_back(sh.na * sh.nb);
+    std::sort(caps.begin(), caps.end());
+    caps.erase(std::unique(caps.begin(), caps.end()), caps.end());
+    std::vector<int> best;
+    double best_est = 0.0;
+    for (int cap : caps) {
+        double e = 0.0;
+        std::vector<int> sh = choose_shapes_capped(dims, num_cus, cap, &e);
+        if (best.empty() || e < best_est * 0.999) {
+            best = sh;
+            best_est = e;
         }
     }
-    S.makespan = num_wgs ? *std::max_element(wload.begin(), wload.end()) : 0.0;
-    return S;
+    if (est) *est = best_est;
+    return best;
 }
 
 }  // namespace
@@ -160,27 +271,11 @@ extern "C" const char* nvfp4_gg_status_string(nvfp4_gg_status_t s)
     case NVFP4_GG_OK: return "success";
     case NVFP4_GG_EINVAL: return "invalid argument";
     case NVFP4_GG_EALIGN: return "device pointer not 16-byte aligned";
-    case NVFP4_GG_ENOMEM: return "host or device allocation failed";
+    case NVFP4_GG_ENOMEM: return "host allocation failed";
     case NVFP4_GG_EHIP: return "HIP runtime error";
     case NVFP4_GG_EUNSUPPORTED: return "unsupported device or configuration";
     }
     return "unknown status";
-}
-
-// Free the plan's device schedule on its device, after that device has finished the work
-// already enqueued (a launch may still be reading the schedule).
-static void free_device(nvfp4_gg_plan_s* p)
-{
-    if (p->d_tiles == nullptr && p->d_wg_begin == nullptr) return;
-    int prev = -1;
-    const bool switch_dev = hipGetDevice(&prev) == hipSuccess && prev != p->device;
-    if (switch_dev) (void)hipSetDevice(p->device);
-    (void)hipDeviceSynchronize();
-    if (p->d_tiles) (void)hipFree(p->d_tiles);
-    if (p->d_wg_begin) (void)hipFree(p->d_wg_begin);
-    if (switch_dev) (void)hipSetDevice(prev);
-    p->d_tiles = nullptr;
-    p->d_wg_begin = nullptr;
 }
 
 extern "C" nvfp4_gg_status_t nvfp4_gg_plan(nvfp4_gg_plan_t* out, int g, const int* m, int n, int k, int device)
@@ -233,12 +328,6 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g,
         p->device = device;
         p->num_cus = num_cus;
         p->scale_layout = scale_layout;
-        bool all256 = true;
-        for (int i = 0; i < g; ++i) all256 = all256 && (problems[i].k % 256) == 0;
-        p->variant = scale_layout == NVFP4_GG_SCALES_BLOCKED ? kVariantPersistentBlocked
-                     : all256                                ? kVariantPersistent
-                                                             : kVariantPersistentKTail;
-        p->shape = variant_shape(p->variant);
         p->m.resize(g);
         p->ns.resize(g);
         p->ks.resize(g);
@@ -261,76 +350,33 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_problems(nvfp4_gg_plan_t* out, int g,
         p->order.resize(g);
         std::iota(p->order.begin(), p->order.end(), 0);
         std::stable_sort(p->order.begin(), p->order.end(), [&](int a, int b) { return work(a) > work(b); });
-        std::vector<int> m_sched(g), n_sched(g), k_sched(g);
-        for (int s = 0; s < g; ++s) {
-            m_sched[s] = p->m[p->order[s]];
-            n_sched[s] = p->ns[p->order[s]];
-            k_sched[s] = p->ks[p->order[s]];
-        }
+        std::vector<GroupDims> dims(g);
+        for (int s = 0; s < g; ++s) dims[s] = GroupDims{p->m[p->order[s]], p->ns[p->order[s]], p->ks[p->order[s]]};
 
-        // pick the chunk height with the smallest estimated makespan
-        Schedule best;
-        bool have = false;
-        for (int R : {96, 64, 32}) {
-            Schedule S = build_schedule(R, m_sched, n_sched, k_sched, num_cus);
-            if (!have || S.makespan < best.makespan * 0.999) {
-                best = std::move(S);
-                have = true;
+        const std::vector<int> shape = choose_shapes(dims, num_cus, &p->est_cycles);
+        long units = 0;
+        int vq = 0;
+        (void)makespan(dims, shape, num_cus, &units, &vq);
+        if (units > 0x7fffffffL) {
+            delete p;
+            return NVFP4_GG_EUNSUPPORTED;
+        }
+        p->units = (int)units;
+        p->vq = vq;
+        p->grid = kXcds * vq;
+        p->na.assign(g, 0);
+        p->nb.assign(g, 0);
+        p->unit_begin.assign(g + 1, 0);
+        for (int s = 0; s < g; ++s) {
+            if (shape[s] >= 0) {
+                p->na[s] = kShapes[shape[s]].na;
+                p->nb[s] = kShapes[shape[s]].nb;
             }
-        }
-        p->chunk_rows = best.chunk_rows;
-        p->est_cycles = best.makespan;
-
-        // flatten: tiles[b] is the first tile of workgroup b (rows = 0 if it has none), so
-        // that a workgroup can fetch it without first reading its range; the further tiles
-        // of workgroup b follow at tiles[wg_begin[b] .. wg_begin[b+1]).  The grid ends at the
-        // last busy workgroup.
-        int last = -1;
-        for (int b = 0; b < num_cus; ++b)
-            if (!best.per_wg[b].empty()) last = b;
-        p->grid = last + 1;
-        p->tiles.assign(p->grid, TileDesc{0, 0, 0, 0});
-        p->wg_begin.assign(p->grid + 1, p->grid);
-        for (int b = 0; b < p->grid; ++b) {
-            const auto& v = best.per_wg[b];
-            if (!v.empty()) p->tiles[b] = v[0];
-            p->wg_begin[b] = (int)p->tiles.size();
-            for (size_t i = 1; i < v.size(); ++i) p->tiles.push_back(v[i]);
-        }
-        p->wg_begin[p->grid] = (int)p->tiles.size();
-        p->total_tiles = 0;
-        for (const auto& t : p->tiles) p->total_tiles += t.rows > 0 ? 1 : 0;
-
-        // informational per-group tile prefix (schedule order)
-        p->tile_begin.assign(g + 1, 0);
-        for (int s = 0; s < g; ++s) {
-            const int chunks = m_sched[s] ? ceil_div(m_sched[s], p->chunk_rows) : 0;
-            p->tile_begin[s + 1] = p->tile_begin[s] + chunks * ceil_div(n_sched[s], kTileCols);
+            p->unit_begin[s + 1] = p->unit_begin[s] + (shape[s] >= 0 ? (int)group_units(dims[s], kShapes[shape[s]]) : 0);
         }
     } catch (...) {
         delete p;
         return NVFP4_GG_ENOMEM;
-    }
-
-    if (device != NVFP4_GG_DEVICE_NONE && p->total_tiles > 0) {
-        int prev = -1;
-        if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess) {
-            delete p;
-            return NVFP4_GG_EHIP;
-        }
-        bool ok = hipMalloc(reinterpret_cast<void**>(&p->d_tiles), sizeof(TileDesc) * p->tiles.size()) == hipSuccess &&
-                  hipMalloc(reinterpret_cast<void**>(&p->d_wg_begin), sizeof(int) * p->wg_begin.size()) == hipSuccess;
-        ok = ok &&
-             hipMemcpy(p->d_tiles, p->tiles.data(), sizeof(TileDesc) * p->tiles.size(), hipMemcpyHostToDevice) ==
-                 hipSuccess &&
-             hipMemcpy(p->d_wg_begin, p->wg_begin.data(), sizeof(int) * p->wg_begin.size(), hipMemcpyHostToDevice) ==
-                 hipSuccess;
-        (void)hipSetDevice(prev);
-        if (!ok) {
-            free_device(p);
-            delete p;
-            return NVFP4_GG_ENOMEM;
-        }
     }
     *out = p;
     return NVFP4_GG_OK;
@@ -346,12 +392,14 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
     KernArgs args;
     std::memset(&args, 0, sizeof(args));
     args.g = plan->g;
-    args.ntiles = plan->total_tiles;
+    args.units = plan->units;
+    args.vq = plan->vq;
+    args.flags = plan->scale_layout == NVFP4_GG_SCALES_BLOCKED ? kFlagBlockedScales : 0;
     for (int s = 0; s < plan->g; ++s) {
         const int i = plan->order[s];
         const int mi = plan->m[i];
         GroupArgs& G = args.grp[s];
-        G.m = mi;
+        G.m_shape = mi | (plan->na[s] << kNaShift) | (plan->nb[s] << kNbShift);
         G.n = plan->ns[i];
         G.k = plan->ks[i];
         G.ldc = plan->ldcs[i];
@@ -371,11 +419,8 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_run(nvfp4_gg_plan_t plan, const void* cons
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return NVFP4_GG_EHIP;
     if (cur != plan->device) return NVFP4_GG_EINVAL;
-    if (plan->total_tiles == 0) return NVFP4_GG_OK;
-
-    args.tiles = plan->d_tiles;
-    args.wg_begin = plan->d_wg_begin;
-    if (launch_variant(plan->variant, args, plan->grid, stream) != hipSuccess) return NVFP4_GG_EHIP;
+    if (plan->units == 0) return NVFP4_GG_OK;
+    if (launch_units(args, plan->grid, stream) != hipSuccess) return NVFP4_GG_EHIP;
     return NVFP4_GG_OK;
 }
 
@@ -388,16 +433,21 @@ extern "C" nvfp4_gg_status_t nvfp4_gg_plan_info(nvfp4_gg_plan_t plan, nvfp4_gg_p
     info->k = plan->k;
     info->device = plan->device;
     info->num_cus = plan->num_cus;
-    info->tile_m = plan->chunk_rows;
-    info->tile_n = kTileCols;
-    info->total_tiles = plan->total_tiles;
+    for (int s = 0; s < plan->g; ++s) {
+        info->tile_m = std::max(info->tile_m, 32 * plan->na[s]);
+        info->tile_n = std::max(info->tile_n, 32 * plan->nb[s]);
+        info->unit_rows[s] = 32 * plan->na[s];
+        info->unit_cols[s] = 32 * plan->nb[s];
+    }
+    info->total_tiles = plan->units;
     info->grid = plan->grid;
-    info->block = plan->shape.block;
-    info->lds_bytes = plan->shape.lds_bytes;
-    info->variant = plan->variant;
+    info->block = kUnitThreads;
+    info->lds_bytes = kUnitLdsBytes;
+    info->variant = plan->scale_layout == NVFP4_GG_SCALES_BLOCKED ? 6 : 5;
     for (int s = 0; s < plan->g; ++s) info->order[s] = plan->order[s];
-    for (int s = 0; s <= plan->g; ++s) info->tile_begin[s] = plan->tile_begin[s];
+    for (int s = 0; s <= plan->g; ++s) info->tile_begin[s] = plan->unit_begin[s];
     info->scale_layout = plan->scale_layout;
+    info->est_us = plan->est_cycles / 2.1e3;
     return NVFP4_GG_OK;
 }
 
@@ -422,6 +472,5 @@ extern "C" void nvfp4_gg_destroy(nvfp4_gg_plan_t plan)
 {
     if (!plan_ok(plan)) return;
     plan->magic = 0;
-    free_device(plan);
     delete plan;
 }

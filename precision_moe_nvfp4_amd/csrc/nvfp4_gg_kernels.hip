@@ -11,28 +11,32 @@
 // 6 significant bits and magnitude in [2^-10, 2688], so it is an exact normal fp16
 // number, and the contraction runs on the fp16 MFMA with fp32 sums.
 //
-// Structure: a persistent grid (one workgroup of 8 waves, 2 per SIMD, per CU) walks a tile
-// list built by the host planner.  A tile is up to 96 rows of one group x 128 columns.
-// Wave w owns the 64 columns 64 (w & 1) .. +64 and all tile rows, and one quarter of every
-// K step (w >> 1); the four partial sums of a column half are added through LDS at the
-// end.  So each dequantised B fragment feeds one MFMA per 32 tile rows, and each A
-// fragment feeds two MFMAs:
-//   * An LDS ring receives, per superstep of K = 256, the raw bytes of the superstep (B
-//     rows, A rows and their scales) straight from HBM through direct-to-LDS loads (no
-//     VGPR staging), one whole 128-byte line per row and load instruction; LDS holds
-//     nothing else, so 5 to 7 slots fit and 3 to 5 supersteps stay in flight.
-//   * Every wave reads the raw bytes of its own K quarter of both operands from the ring
-//     and dequantises them in registers into MFMA fragments, one half superstep ahead of
-//     their use, while the MFMAs of the current half run.
-//   * One barrier per superstep both publishes the next superstep's slot and frees the
-//     slot just consumed, which is refilled at once.
-//   * v_mfma_f32_32x32x16_f16 takes the B fragment as its M-side operand, so each lane
-//     ends up holding runs of 4 consecutive C columns (8-byte fp16 stores).
-// K is permuted inside each half superstep, identically for A and B (the dot product is
-// unchanged): lane half h, K quarter t and step u take the 8 K values starting at
-// 64h + 16t + 8u, so that a lane's bytes of a whole half are 8 contiguous bytes.
+// Structure.  One workgroup of 4 waves (one per SIMD) per CU walks a range of work units;
+// a unit is up to 32*NA rows of one group times 32*NB columns, over the whole K.  Every
+// wave owns the whole unit tile (NB x NA blocks of 32x32 fp32 accumulators, kept in the
+// accumulation registers) and one quarter of every K superstep:
+//   * K runs in supersteps of 256 (128 bytes of codes per row: one cache line).  The four
+//     waves together fetch a superstep's lines (A and B codes, both scale sets) straight
+//     from HBM/L2 into a ring slot in LDS (direct-to-LDS buffer loads, one whole line per
+//     8 lanes); a 4- to 6-slot ring keeps 2-4 supersteps in flight.
+//   * Wave w consumes K values 64w .. 64w+63 of each superstep: each lane reads its 16
+//     code bytes per 32-row block with one LDS read (rows are stored with an XOR swizzle
+//     of their 16-byte chunks, so the reads are bank-conflict free) and its two scale
+//     bytes, converts them to MFMA fragments in registers and issues the MFMAs.  No LDS
+//     holds converted values, so each FP4 byte is converted exactly once per unit.
+//   * One barrier per superstep publishes the next superstep and frees the slot that was
+//     read during the previous one.
+//   * At the end of a unit the four K-quarter partial sums are added through LDS, rounded
+//     to fp16 and stored.
+// v_mfma_f32_32x32x16_f16 takes a B fragment (32 columns of C) as its first operand and
+// an A fragment (32 rows of C) as its second, so a lane ends up holding runs of 4
+// consecutive columns of one C row.  Inside each 64-K quarter the K order is permuted
+// identically for A and B (the dot product is unchanged): lane half h, step s takes the
+// 8 K values 64w + 32h + 8s .. +8, so a lane's 16 bytes are contiguous in the row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "nvfp4_gg_internal.h"
 
@@ -45,7 +49,7 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------------
-// Exact dequantisation helpers
+// Exact dequantisation
 // ---------------------------------------------------------------------------------------
 
 // fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 under the default mode).
@@ -56,799 +60,612 @@ __device__ __forceinline__ uint16_t f16_bits_rne(float f)
 }
 
 // 8 E2M1 codes (nibble i = element i, i.e. low nibble = even K) times one fp16 scale ->
-// 4 dwords of fp16 pairs (element 2j in the low half of dword j).  The hardware FP4 ->
-// fp16 conversion with scale 1.0 gives the exact E2M1 values; one packed fp16 multiply
-// per pair applies the E4M3 scale exactly.
-__device__ __forceinline__ u4_t dequant8(uint32_t x, h2_t s)
+// one MFMA fragment (element 2j in the low half of dword j).  The hardware FP4 -> fp16
+// conversion with scale 1.0 gives the exact E2M1 values; one packed fp16 multiply per
+// pair applies the E4M3 scale exactly.
+__device__ __forceinline__ h8_t dequant8(uint32_t x, h2_t s)
 {
     u4_t o;
     o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s);
     o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s);
     o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s);
     o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s);
-    return o;
+    return __builtin_bit_cast(h8_t, o);
 }
 
 // ---------------------------------------------------------------------------------------
-// Geometry and LDS layout
+// Geometry
 // ---------------------------------------------------------------------------------------
-namespace pk {
-constexpr int THREADS = 512;         // 8 waves, 2 per SIMD
-constexpr int BN = 128;              // tile columns: wave w owns columns 64 (w & 1) .. +64
-constexpr int RMAX = 96;             // tile rows (multiple of 32)
-
-constexpr int SK = 256;              // K per load superstep
-constexpr int ROWB = SK / 2;         // code bytes per row and superstep: one 128-byte line
-constexpr int SCB = SK / 16;         // scale bytes per row and superstep
-constexpr int MAX_SLOTS = 7;
+namespace gk {
+constexpr int THREADS = 256;           // 4 waves, one per SIMD
+constexpr int SK = 256;                // K per superstep
+constexpr int ROWB = SK / 2;           // code bytes per row and superstep: one 128-byte line
+constexpr int BLK_CODE = 32 * ROWB;    // one 32-row block's codes per superstep (4 KiB)
 constexpr int LDS_BYTES = 160 * 1024;
-// LDS holds only the ring: ring_slots(rpad) slots of slot_bytes(rpad) for a tile with rpad
-// rows, each holding the raw bytes of one superstep (all offsets multiples of 16 bytes):
-//     B codes   128 rows x 128 B   at 0            (16-byte chunk c of row r at c ^ swz(r))
-//     B scales  128 rows x 16 B    at B_SCALES_AT
-//     A codes   rpad rows x 128 B  at A_CODES_AT   (same chunk swizzle)
-//     A scales  rpad rows x 16 B   at A_CODES_AT + 128 rpad
-// (5 slots of 96-row tiles, 5 of 64-row tiles, 7 of 32-row tiles).  Whole 128-byte lines
-// per row and load instruction: a wave's 16-byte lanes cover 8 rows per instruction
-// instead of 32, which is what lets a CU pull shared operand rows out of L2 at ~3x the
-// rate of 32-byte row pieces.
-// Chunk swizzle of the raw rows: the 3-bit reversal of (r >> 1) & 7, so that the 8-byte
-// reads of one chunk half from 32 consecutive rows spread over 16 chunk positions.
-__host__ __device__ constexpr int swz(int r)
-{
-    return (((r >> 1) & 1) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1);
-}
-constexpr int B_SCALES_AT = BN * ROWB;                // 16384
-constexpr int A_CODES_AT = B_SCALES_AT + BN * SCB;    // 18432
-__host__ __device__ constexpr int slot_bytes(int rpad) { return A_CODES_AT + rpad * (ROWB + SCB); }
-__host__ __device__ constexpr int ring_slots(int rpad)
-{
-    return LDS_BYTES / slot_bytes(rpad) > MAX_SLOTS ? MAX_SLOTS : LDS_BYTES / slot_bytes(rpad);
-}
-// reduction area (overlays the ring after the last superstep): per wave, for each column
-// block and 32-row block, the three element groups handed to the other K quarters (one u4
-// per lane each)
-constexpr int RED_WAVE = 2 * (RMAX / 32) * 3 * 64 * 16;
-// staged output rows of the epilogue (fp16, 128 columns, padded to spread banks)
-constexpr int STAGE_ROW = BN * 2 + 16;
-static_assert(RMAX * STAGE_ROW <= LDS_BYTES, "staged output tile must fit in LDS");
-static_assert(ring_slots(RMAX) >= 3, "the tallest tile needs at least 3 ring slots");
-static_assert(8 * RED_WAVE <= LDS_BYTES, "reduction area must fit in LDS");
-}  // namespace pk
+constexpr int MAX_SLOTS = 6;
+
+// Chunk swizzle: row r of a block keeps its 16-byte chunk c at position c ^ swz(r).  The
+// 16-byte reads of one chunk from rows 0..7 (or 0..15) of a block then fall on distinct
+// bank groups for 32 banks (8 lanes per cycle) and for 64 banks (16 lanes per cycle).
+__host__ __device__ constexpr int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Ring slot of a unit with NA row blocks (A) and NB column blocks (B):
+//   codes   block x (B blocks 0..NB-1, then A blocks NB..NB+NA-1): 32 rows x 128 B at
+//           x * 4096, row r at 128 r, chunk c at 16 (c ^ swz(r));
+//   scales  four row-quarter regions (rows 8q..8q+7 of every block, loaded by wave q),
+//           SREG bytes apart; inside region q, scale block y (B blocks 0..NB-1, then A
+//           blocks from NBp = NB rounded up to even) row 8q + i: 16 bytes at 128 y + 16 i.
+//           The regions are 4 bytes more than a multiple of 256 apart, so that the scale
+//           reads of rows 0..31 (one dword each) fall on 32 distinct banks.
+template <int NA, int NB>
+struct Geo {
+    static constexpr int NBLK = NA + NB;
+    static constexpr int NBP = (NB + 1) & ~1;
+    static constexpr int NAP = (NA + 1) & ~1;
+    static constexpr int SREG = 128 * (NBP + NAP) + 4;
+    static constexpr int SCALE_AT = NBLK * BLK_CODE;
+    static constexpr int SLOT = (SCALE_AT + 4 * SREG + 15) & ~15;
+    static constexpr int SLOTS = LDS_BYTES / SLOT > MAX_SLOTS ? MAX_SLOTS : LDS_BYTES / SLOT;
+    static constexpr int NSI = (NBP + NAP) / 2;    // scale load instructions per wave
+    static constexpr int OPS = NBLK + NSI;         // loads per wave and superstep
+    static constexpr int NACC = NA * NB;           // accumulator blocks
+    // epilogue exchange: per block, 4 element groups x 3 partner copies x 1 KiB
+    static constexpr int RED_BLK = 3 * 4 * 1024;
+    static constexpr int RED_ROUND = (LDS_BYTES / RED_BLK) < NACC ? (LDS_BYTES / RED_BLK) : NACC;
+    static_assert(SLOTS >= 3, "a unit shape needs at least 3 ring slots");
+    static_assert((SLOTS - 2) * OPS <= 63, "the steady-state wait count must fit vmcnt");
+};
+}  // namespace gk
 
 // ---------------------------------------------------------------------------------------
 // Loads
 // ---------------------------------------------------------------------------------------
 
-// How the scales are fetched (see SuperLoads).
-enum ScaleMode : int {
-    SCL_ROW16 = 0,    // row-major scales, 16 bytes per lane (k % 256 == 0: 16-byte rows)
-    SCL_BLOCKED = 1,  // 128x4 blocked scales, 4 bytes per lane
-    SCL_ROW4 = 2,     // row-major scales, 4 bytes per lane (rows only 4-byte aligned)
+// Raw buffer resource over `bytes` bytes at base (at most 2^31 - 1): loads address it as
+// scalar base + 32-bit vector offset + scalar offset, and offsets at or beyond `bytes`
+// read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, long bytes)
+{
+    const int n = bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voff, soff, 0, 0);
+}
+
+// What one wave loads for one unit, per superstep (addresses relative to the unit):
+//   codes: for every block, the 8 rows 8w .. 8w+7 (lane l: row 8w + l/8, global chunk
+//          (l%8) ^ swz(row), stored at LDS chunk position l%8);
+//   scales: for every pair of scale blocks, rows 8w .. 8w+7 x the superstep's four 4-byte
+//          scale words (lane l: block 2p + l/32, row 8w + (l%32)/4, word l%4).
+// B rows beyond n and A rows beyond m read as zero codes (buffer range); their scale rows
+// are clamped to the last row, so that padding scales are never read.
+template <int NA, int NB>
+struct UnitLoads {
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+    uint32_t code[(NA > NB ? NA : NB)];       // per-lane code offset of block b' of a side
+    uint32_t scl[gk::Geo<NA, NB>::NSI];       // per-lane scale offset of scale instruction p
+    int scl_step;                             // scale bytes between supersteps
+    int code_chunk;                           // global 16-byte chunk of this lane's code loads
+    int scl_word;                             // scale word (0..3) of this lane's scale loads
 };
 
-// Per-wave direct-to-LDS loads of one superstep.  B code instruction i (rows 8i .. +8,
-// i < 16) goes to wave i % 8 and A code instruction a (rows 8a .. +8) to wave (a + 4) % 8.
-// Scales, SCL_ROW16: B scale instruction q (rows 32q .. +32, 16 bytes per lane, lanes < 32)
-// to wave q < 4, A scale instruction q to wave 7 - q.  Scales, SCL_BLOCKED and SCL_ROW4:
-// 4 bytes per lane, so instruction q covers rows 16q .. +16 (lane l: row 16q + l / 4,
-// scale dword l % 4 of the superstep); B scale instruction q to wave q (all 8), A scale
-// instruction q to wave q.  Either way the LDS copy of a superstep's scales is the same:
-// row r's 16 bytes at 16 r.  In a last superstep that holds fewer than 256 K values, lanes
-// whose code chunk or scale dword lies beyond K store zeros to their LDS place instead of
-// loading (zero codes and zero scales contribute exact zeros); every instruction keeps at
-// least one loading lane, so the per-superstep load count is unchanged.
-// Source addresses are a workgroup-uniform base (first row of the tile, superstep 0) plus a
-// 32-bit per-lane offset, so that the loads address memory as scalar base + vector offset
-// and the per-superstep advance is a scalar add.
-struct SuperLoads {
-    const uint8_t* bb;    // B codes: uniform base
-    const uint8_t* sbb;   // B scales: uniform base
-    const uint8_t* ab;    // A codes: uniform base
-    const uint8_t* sab;   // A scales: uniform base
-    __amdgpu_buffer_rsrc_t rb, rsb, ra, rsa;   // buffer resources of the four bases
-    uint32_t b[2];        // this lane's offsets from the bases
-    uint32_t sb;
-    uint32_t a[2];
-    uint32_t sa;
-    int b_dst[2];         // LDS offsets (inside a slot) of the B code instructions
-    int sb_dst;
-    int a_dst[2];
-    int sa_dst;
-    int nsb;              // B scale instructions of this wave (0 or 1)
-    int na;               // A code instructions of this wave (0 .. 2)
-    int nsa;              // A scale instructions of this wave (0 or 1)
-    int ops;              // loads per superstep issued by this wave
-    int b_chunk[2];       // global 16-byte chunk (0 .. 7) of a row that this lane loads
-    int a_chunk[2];
-    int s_dword;          // scale dword (0 .. 3) of the superstep this lane loads (4-byte modes)
-    long sstride;         // scale bytes between consecutive supersteps of this lane
-};
-
-// Loads per superstep issued by wave w for tiles of 32 nrb rows (the assignment above).
-__host__ __device__ constexpr int pk_ops(int w, int nrb, bool blocked)   // blocked: 4-byte scale loads
+// Issue wave w's loads of superstep t (kt = K values it holds: 256 except maybe in the
+// last) into `slot`.  In a short superstep, lanes whose 16-byte code chunk or 4-byte scale
+// word lies beyond K store zeros to their LDS place instead of loading (zero codes and
+// zero scales add exact zeros); every instruction keeps loading lanes, so the number of
+// loads per superstep, and with it every wait count, is the same in all supersteps.
+template <int NA, int NB>
+__device__ __forceinline__ void issue_superstep(const UnitLoads<NA, NB>& L, uint8_t* slot, int t, int kt, int wave,
+                                                int lane)
 {
-    int ops = 2;                                            // B codes: instructions w, w + 8
-    ops += blocked ? 1 : (w < 4 ? 1 : 0);                   // B scales
-    for (int q = 0; q < 2; ++q) ops += ((w + 4) & 7) + 8 * q < 4 * nrb ? 1 : 0;   // A codes
-    ops += blocked ? (w < 2 * nrb ? 1 : 0) : (7 - w < nrb ? 1 : 0);             // A scales
-    return ops;
-}
-__host__ __device__ constexpr int pk_ops_min(int nrb, bool blocked)
-{
-    int v = pk_ops(0, nrb, blocked);
-    for (int w = 1; w < 8; ++w) v = pk_ops(w, nrb, blocked) < v ? pk_ops(w, nrb, blocked) : v;
-    return v;
-}
-__host__ __device__ constexpr int pk_ops_max(int nrb, bool blocked)
-{
-    int v = pk_ops(0, nrb, blocked);
-    for (int w = 1; w < 8; ++w) v = pk_ops(w, nrb, blocked) > v ? pk_ops(w, nrb, blocked) : v;
-    return v;
-}
-
-// Raw buffer resource over [base, base + 2^31): loads address it as scalar base + 32-bit
-// vector offset + scalar offset, so the per-lane part needs no 64-bit address arithmetic
-// and the per-superstep advance rides in the scalar offset.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t pk_rsrc(const uint8_t* base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7fffffff, 0x00020000);
-}
-
-// Direct-to-LDS buffer loads of 16 / 4 bytes per lane at voff + soff into lds_base + 16 (4)
-// times the lane index.
-__device__ __forceinline__ void pk_bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, soff,
-                                             0, 0);
-}
-__device__ __forceinline__ void pk_bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voff, soff,
-                                             0, 0);
-}
-
-// 16 code bytes of this lane, or zeros when its chunk lies beyond the superstep's K.
-__device__ __forceinline__ void pk_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds_base,
-                                          int lane, bool valid)
-{
-    if (valid) {
-        pk_bload16(r, voff, soff, lds_base);
+    using G = gk::Geo<NA, NB>;
+    const int soff = t * gk::ROWB;
+    const int ssoff = t * L.scl_step;
+    if (kt == gk::SK) {
+#pragma unroll
+        for (int x = 0; x < NB; ++x) dma16(L.rb, L.code[x], soff, slot + x * gk::BLK_CODE + wave * 1024);
+#pragma unroll
+        for (int x = 0; x < NA; ++x) dma16(L.ra, L.code[x], soff, slot + (NB + x) * gk::BLK_CODE + wave * 1024);
+#pragma unroll
+        for (int p = 0; p < G::NSI; ++p)
+            dma4(p < G::NBP / 2 ? L.rsb : L.rsa, L.scl[p], ssoff, slot + G::SCALE_AT + wave * G::SREG + p * 256);
     } else {
-        *reinterpret_cast<u4_t*>(lds_base + 16 * lane) = u4_t{0u, 0u, 0u, 0u};
+        const bool cv = L.code_chunk < (kt >> 5);
+        const bool sv = L.scl_word < (kt >> 6);
+#pragma unroll
+        for (int x = 0; x < G::NBLK; ++x) {
+            uint8_t* dst = slot + x * gk::BLK_CODE + wave * 1024;
+            if (cv)
+                dma16(x < NB ? L.rb : L.ra, L.code[x < NB ? x : x - NB], soff, dst);
+            else
+                *reinterpret_cast<u4_t*>(dst + 16 * lane) = u4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int p = 0; p < G::NSI; ++p) {
+            uint8_t* dst = slot + G::SCALE_AT + wave * G::SREG + p * 256;
+            if (sv)
+                dma4(p < G::NBP / 2 ? L.rsb : L.rsa, L.scl[p], ssoff, dst);
+            else
+                *reinterpret_cast<uint32_t*>(dst + 4 * lane) = 0u;
+        }
     }
 }
 
-// Issue the loads of superstep t (kt = K values it holds, 256 except maybe in the last).
-template <int SCL>
-__device__ __forceinline__ void pk_issue(uint8_t* slot_base, int t, int kt, const SuperLoads& L, int lane)
+// Per-lane load offsets and buffer resources of one unit (see UnitLoads).  `rows` / `cols`
+// are the unit's valid A rows / B rows (C columns).
+template <int NA, int NB>
+__device__ __forceinline__ UnitLoads<NA, NB> unit_loads(const GroupArgs& G, int k, int row0, int rows, int col0,
+                                                        int cols, bool blocked, int wave, int lane)
 {
-    using namespace pk;
-    const int kb = t * ROWB;                      // scalar offsets of superstep t
-    const int ks = t * (int)L.sstride;
-    if (SCL == SCL_ROW16 || kt == SK) {   // (SCL_ROW16 plans have no short supersteps)
-        pk_bload16(L.rb, L.b[0], kb, slot_base + L.b_dst[0]);
-        pk_bload16(L.rb, L.b[1], kb, slot_base + L.b_dst[1]);
-        if constexpr (SCL == SCL_ROW16) {
-            if (L.nsb > 0 && lane < 32) pk_bload16(L.rsb, L.sb, ks, slot_base + L.sb_dst);
-            if (L.nsa > 0 && lane < 32) pk_bload16(L.rsa, L.sa, ks, slot_base + L.sa_dst);
-        } else {
-            if (L.nsb > 0) pk_bload4(L.rsb, L.sb, ks, slot_base + L.sb_dst);
-            if (L.nsa > 0) pk_bload4(L.rsa, L.sa, ks, slot_base + L.sa_dst);
+    using Gm = gk::Geo<NA, NB>;
+    UnitLoads<NA, NB> L;
+    const long qs = k / 2;
+    const int rb8 = 8 * wave + (lane >> 3);   // row inside a block of this lane's code loads
+    L.code_chunk = (lane & 7) ^ gk::swz(rb8);
+#pragma unroll
+    for (int b = 0; b < (NA > NB ? NA : NB); ++b) L.code[b] = (uint32_t)((32 * b + rb8) * qs + 16 * L.code_chunk);
+    L.rb = make_rsrc(G.b + (long)col0 * qs, (long)cols * qs);
+    L.ra = make_rsrc(G.a + (long)row0 * qs, (long)rows * qs);
+    L.scl_word = lane & 3;
+    const int srow = 8 * wave + ((lane & 31) >> 2);   // row inside a block of this lane's scale loads
+    if (!blocked) {
+        // row-major [rows][k/16]: superstep t's 16 scales of a row are its bytes 16t .. 16t+15
+        const long ss = k / 16;
+#pragma unroll
+        for (int p = 0; p < Gm::NSI; ++p) {
+            const int y = 2 * p + (lane >> 5);
+            const bool bside = p < Gm::NBP / 2;
+            const int bl = bside ? min(y, NB - 1) : min(y - Gm::NBP, NA - 1);
+            const int r = min(32 * bl + srow, (bside ? cols : rows) - 1);
+            L.scl[p] = (uint32_t)(r * ss + 4 * L.scl_word);
         }
-        if (L.na > 0) pk_bload16(L.ra, L.a[0], kb, slot_base + L.a_dst[0]);
-        if (L.na > 1) pk_bload16(L.ra, L.a[1], kb, slot_base + L.a_dst[1]);
+        L.rsb = make_rsrc(G.sfb + (long)col0 * ss, 0x7fffffffL);
+        L.rsa = make_rsrc(G.sfa + (long)row0 * ss, 0x7fffffffL);
+        L.scl_step = gk::SK / 16;
     } else {
-        // a short last superstep: kt / 32 code chunks and kt / 64 scale dwords per row
-        const int vchunks = kt >> 5, vdw = kt >> 6;
-        pk_load16(L.rb, L.b[0], kb, slot_base + L.b_dst[0], lane, L.b_chunk[0] < vchunks);
-        pk_load16(L.rb, L.b[1], kb, slot_base + L.b_dst[1], lane, L.b_chunk[1] < vchunks);
-        if constexpr (SCL != SCL_ROW16) {
-            const bool sv = L.s_dword < vdw;
-            if (L.nsb > 0) {
-                if (sv) pk_bload4(L.rsb, L.sb, ks, slot_base + L.sb_dst);
-                else *reinterpret_cast<uint32_t*>(slot_base + L.sb_dst + 4 * lane) = 0u;
-            }
-            if (L.nsa > 0) {
-                if (sv) pk_bload4(L.rsa, L.sa, ks, slot_base + L.sa_dst);
-                else *reinterpret_cast<uint32_t*>(slot_base + L.sa_dst + 4 * lane) = 0u;
-            }
+        // 128x4 blocked: scale (row R, K block c) at ((R/128) (k/64) + c/4) 512 + 16 (R%32)
+        // + 4 ((R/32)%4) + c%4; superstep t covers the four atoms 4t .. 4t+3 of a row block
+        const long atoms = k / 64;
+        const int b0 = col0 >> 7, a0 = row0 >> 7;
+#pragma unroll
+        for (int p = 0; p < Gm::NSI; ++p) {
+            const int y = 2 * p + (lane >> 5);
+            const bool bside = p < Gm::NBP / 2;
+            const int bl = bside ? min(y, NB - 1) : min(y - Gm::NBP, NA - 1);
+            const int r = min(32 * bl + srow, (bside ? cols : rows) - 1);
+            const int R = (bside ? col0 : row0) + r;
+            const int rb0 = bside ? b0 : a0;
+            L.scl[p] = (uint32_t)((((long)(R >> 7) - rb0) * atoms + L.scl_word) * 512 + 16 * (R & 31) +
+                                  4 * ((R >> 5) & 3));
         }
-        if (L.na > 0) pk_load16(L.ra, L.a[0], kb, slot_base + L.a_dst[0], lane, L.a_chunk[0] < vchunks);
-        if (L.na > 1) pk_load16(L.ra, L.a[1], kb, slot_base + L.a_dst[1], lane, L.a_chunk[1] < vchunks);
+        L.rsb = make_rsrc(G.sfb + (long)b0 * atoms * 512, 0x7fffffffL);
+        L.rsa = make_rsrc(G.sfa + (long)a0 * atoms * 512, 0x7fffffffL);
+        L.scl_step = 4 * 512;
     }
+    return L;
 }
 
-// Wait until at most n of this wave's loads are in flight (0 <= n <= 30).
-__device__ __forceinline__ void pk_wait_loads(int n)
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vm()
 {
-#define NVFP4GG_WAIT_CASE(N) \
-    case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    static_assert(N >= 0 && N <= 63, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Wait until at most n * OPS of this wave's loads are in flight (0 <= n <= 4).
+template <int OPS>
+__device__ __forceinline__ void wait_supersteps(int n)
+{
     switch (n) {
-        NVFP4GG_WAIT_CASE(30) NVFP4GG_WAIT_CASE(29) NVFP4GG_WAIT_CASE(28) NVFP4GG_WAIT_CASE(27)
-        NVFP4GG_WAIT_CASE(26) NVFP4GG_WAIT_CASE(25) NVFP4GG_WAIT_CASE(24) NVFP4GG_WAIT_CASE(23)
-        NVFP4GG_WAIT_CASE(22) NVFP4GG_WAIT_CASE(21) NVFP4GG_WAIT_CASE(20) NVFP4GG_WAIT_CASE(19)
-        NVFP4GG_WAIT_CASE(18) NVFP4GG_WAIT_CASE(17) NVFP4GG_WAIT_CASE(16) NVFP4GG_WAIT_CASE(15)
-        NVFP4GG_WAIT_CASE(14) NVFP4GG_WAIT_CASE(13) NVFP4GG_WAIT_CASE(12) NVFP4GG_WAIT_CASE(11)
-        NVFP4GG_WAIT_CASE(10) NVFP4GG_WAIT_CASE(9) NVFP4GG_WAIT_CASE(8) NVFP4GG_WAIT_CASE(7)
-        NVFP4GG_WAIT_CASE(6) NVFP4GG_WAIT_CASE(5) NVFP4GG_WAIT_CASE(4) NVFP4GG_WAIT_CASE(3)
-        NVFP4GG_WAIT_CASE(2) NVFP4GG_WAIT_CASE(1)
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<(OPS <= 63 ? OPS : 63)>(); break;
+    case 2: wait_vm<(2 * OPS <= 63 ? 2 * OPS : 63)>(); break;
+    case 3: wait_vm<(3 * OPS <= 63 ? 3 * OPS : 63)>(); break;
+    default: wait_vm<(4 * OPS <= 63 ? 4 * OPS : 63)>(); break;
     }
-#undef NVFP4GG_WAIT_CASE
 }
 
-// Workgroup barrier for LDS hand-offs: waits for this wave's own LDS reads/writes, then
-// s_barrier.  Unlike __syncthreads() it does not wait for outstanding direct-to-LDS
-// loads (those are waited for explicitly, so later supersteps stay in flight).
+// Workgroup barrier for LDS hand-offs: waits for this wave's own LDS reads and writes, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding direct-to-LDS loads
+// (those are waited for explicitly, so later supersteps stay in flight).
 __device__ __forceinline__ void barrier_lds()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// ---------------------------------------------------------------------------------------
-// Scales
-// ---------------------------------------------------------------------------------------
-
-// fp16 scale pair (column block 0, column block 1) of half HALF: byte 8 HALF + 4h + t of
-// each row's scale bytes, i.e. byte t of the lane's word for that half.
-template <int HALF>
-__device__ __forceinline__ h2_t pk_scales(const u2_t (&srow)[2], uint32_t tsel)
-{
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(srow[1][HALF], srow[0][HALF], tsel), 1.0f,
-                                                    false);
+    // the same wait as an instruction the compiler sees (it cannot read the asm): it then
+    // knows every earlier LDS read has returned and adds no wait of its own for them; the
+    // count is already zero, so this costs nothing
+    __builtin_amdgcn_s_waitcnt(0xc07f);
 }
 
 // ---------------------------------------------------------------------------------------
 // Compute
 // ---------------------------------------------------------------------------------------
 
-// MFMAs of one step: B fragments of the two column blocks, A fragments of the row blocks.
-template <int NRB>
-__device__ __forceinline__ void pk_mfmas(f16v_t (&acc)[2][NRB], const h8_t (&bf)[2], const h8_t (&af)[NRB])
+// This wave's raw code bytes of one half superstep (steps 0-1 or 2-3): 8 bytes per block.
+template <int NA, int NB>
+struct RawHalf {
+    u2_t cb[NB], ca[NA];
+};
+
+// The two scale bytes of each block's row in one superstep (low byte: steps 0 and 1, high
+// byte: steps 2 and 3).
+template <int NA, int NB>
+struct RawScales {
+    uint32_t sb[NB], sa[NA];
+};
+
+template <int NA, int NB, int H>
+__device__ __forceinline__ void read_half(RawHalf<NA, NB>& R, const uint8_t* slot, int code_off)
 {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
+    for (int x = 0; x < NB; ++x) R.cb[x] = *reinterpret_cast<const u2_t*>(slot + x * gk::BLK_CODE + code_off + 8 * H);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-            acc[c][rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[c], af[rb], acc[c][rb], 0, 0, 0);
+    for (int i = 0; i < NA; ++i)
+        R.ca[i] = *reinterpret_cast<const u2_t*>(slot + (NB + i) * gk::BLK_CODE + code_off + 8 * H);
+}
+
+template <int NA, int NB>
+__device__ __forceinline__ void read_scales(RawScales<NA, NB>& R, const uint8_t* slot, int scale_off)
+{
+    using Gm = gk::Geo<NA, NB>;
+#pragma unroll
+    for (int x = 0; x < NB; ++x) R.sb[x] = *reinterpret_cast<const uint16_t*>(slot + Gm::SCALE_AT + scale_off + 128 * x);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+        R.sa[i] = *reinterpret_cast<const uint16_t*>(slot + Gm::SCALE_AT + scale_off + 128 * (Gm::NBP + i));
+}
+
+// MFMA fragments of one 16-K step: one per B block and one per A block.
+template <int NA, int NB>
+struct Frags {
+    h8_t b[NB], a[NA];
+};
+
+// The fp16 scale pairs of a superstep (element 0: steps 0 and 1, element 1: steps 2 and 3).
+template <int NA, int NB>
+struct Scales {
+    h2_t b[NB], a[NA];
+};
+
+template <int NA, int NB>
+__device__ __forceinline__ void convert_scales(Scales<NA, NB>& S, const RawScales<NA, NB>& R)
+{
+#pragma unroll
+    for (int x = 0; x < NB; ++x) S.b[x] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.sb[x], 1.0f, false);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) S.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.sa[i], 1.0f, false);
+}
+
+// Fragments of step ST (0..3) of a superstep from the half that holds it.
+template <int NA, int NB, int ST>
+__device__ __forceinline__ void convert_step(Frags<NA, NB>& F, const RawHalf<NA, NB>& R, const Scales<NA, NB>& S)
+{
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+        const _Float16 c = ST < 2 ? S.b[x].x : S.b[x].y;
+        F.b[x] = dequant8(R.cb[x][ST & 1], h2_t{c, c});
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const _Float16 c = ST < 2 ? S.a[i].x : S.a[i].y;
+        F.a[i] = dequant8(R.ca[i][ST & 1], h2_t{c, c});
+    }
+}
+
+// Accumulator blocks 0..15 (x * NA + i) live in the 256 accumulation registers; a unit with
+// more blocks keeps the rest in ordinary VGPRs.  The compiler places every accumulator of
+// its MFMA builtin in one register class, so the extra blocks use the same instruction
+// written out, with its operands pinned to VGPRs; the s_nop before it covers the VALU
+// writes of its fragments (and of the zero start value) just before, the s_nop after it
+// the reads of its source fragments by the VALU that may overwrite them next.
+constexpr int kAgprBlocks = 16;
+
+__device__ __forceinline__ void mfma_vgpr_acc(f16v_t& acc, const h8_t& b, const h8_t& a)
+{
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 1" : "+v"(acc) : "v"(b), "v"(a));
+}
+
+template <int NA, int NB>
+__device__ __forceinline__ void mfma_step(f16v_t (&acc)[NB][NA], const Frags<NA, NB>& F)
+{
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            if (x * NA + i < kAgprBlocks)
+                acc[x][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.b[x], F.a[i], acc[x][i], 0, 0, 0);
+            else
+                mfma_vgpr_acc(acc[x][i], F.b[x], F.a[i]);
+        }
+}
+
+// After the last MFMA of a unit: the written-out MFMAs' results become readable by the VALU
+// only after the pipeline has drained (the compiler cannot count for them), so wait it out
+// once, with the extra blocks as operands so that no read of them moves above the wait.
+template <int NA, int NB>
+__device__ __forceinline__ void drain_vgpr_acc(f16v_t (&acc)[NB][NA])
+{
+    if constexpr (NA * NB > kAgprBlocks) {
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+                if (x * NA + i >= kAgprBlocks) asm volatile("" : "+v"(acc[x][i]));
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+                if (x * NA + i >= kAgprBlocks) asm volatile("" : "+v"(acc[x][i]));
+    }
+}
+
+// Ask the scheduler to interleave the step's MFMAs with the next step's conversions: one
+// MFMA, then about as many VALU instructions as hide behind it.
+template <int NA, int NB>
+__device__ __forceinline__ void interleave_hint()
+{
+    constexpr int NM = NA * NB;
+    constexpr int NV = 8 * (NA + NB);
+    constexpr int PER = (NV + NM - 1) / NM;
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);   // then VALU
+    }
 }
 
 // ---------------------------------------------------------------------------------------
 // Epilogue
 // ---------------------------------------------------------------------------------------
 
-// Reduction over the four K quarters and store.  Lane (j, h) holds, in acc[c][rb] element
-// 4q + e, the partial sum of C[32 rb + j][64 cw + 32 c + 8 q + 4 h + e].  The wave with K
-// quarter T keeps element group q = T and hands the other three to the waves that keep
-// them (same column half) through LDS.  T is a template parameter so that every element
-// and LDS slot index is static (no register indexing, no per-partner branches) and all
-// partner reads are in flight together.
-template <int NRB, int T>
-__device__ __forceinline__ void pk_reduce_store_q(const f16v_t (&acc)[2][NRB], uint8_t* smem,
-                                                  uint16_t* __restrict__ c0, int n, int ldc, int rows, int col, int wave,
-                                                  int lane)
+// Sum of the four K-quarter partial tiles, fp16 rounding and stores.  Lane (j, h) holds in
+// acc[x][i] element 4q + e the partial sum of C[32 i + j][32 x + 8 q + 4 h + e].  Wave W
+// keeps element group q = W and hands the other three groups to their owners through LDS,
+// RED_ROUND blocks at a time.  W is a template parameter so that every element index is
+// static (the accumulators live in registers that cannot be indexed at run time).
+template <int NA, int NB, int W>
+__device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t* smem, uint16_t* __restrict__ c0,
+                                           int rows, int cols, int ldc, int lane)
 {
-    using namespace pk;
-    const int cw = wave & 1;
-    u4_t* mine = reinterpret_cast<u4_t*>(smem + wave * RED_WAVE);
+    using Gm = gk::Geo<NA, NB>;
+    constexpr int RR = Gm::RED_ROUND;
+    const int j = lane & 31, h = lane >> 5;
+    const bool vec = (ldc & 3) == 0;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int r0 = 0; r0 < Gm::NACC; r0 += RR) {
+        barrier_lds();   // the ring, or the previous round's exchange, is no longer read
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
+        for (int xr = 0; xr < RR && r0 + xr < Gm::NACC; ++xr) {
+            const int xb = (r0 + xr) / NA, ib = (r0 + xr) % NA;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (q == T) continue;
-                const int slot = q - (q > T ? 1 : 0);
-                mine[((c * NRB + rb) * 3 + slot) * 64 + lane] =
-                    u4_t{__float_as_uint(acc[c][rb][4 * q + 0]), __float_as_uint(acc[c][rb][4 * q + 1]),
-                         __float_as_uint(acc[c][rb][4 * q + 2]), __float_as_uint(acc[c][rb][4 * q + 3])};
+                if (q == W) continue;
+                const int slot = W - (W > q ? 1 : 0);
+                *reinterpret_cast<u4_t*>(smem + (((xr * 4 + q) * 3 + slot) * 64 + lane) * 16) =
+                    u4_t{__float_as_uint(acc[xb][ib][4 * q + 0]), __float_as_uint(acc[xb][ib][4 * q + 1]),
+                         __float_as_uint(acc[xb][ib][4 * q + 2]), __float_as_uint(acc[xb][ib][4 * q + 3])};
             }
-    barrier_lds();
-    u4_t o[2][NRB][3];   // group T of the three partner waves
+        }
+        barrier_lds();
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+        for (int xr = 0; xr < RR && r0 + xr < Gm::NACC; ++xr) {
+            const int xb = (r0 + xr) / NA, ib = (r0 + xr) % NA;
+            u4_t o[3];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-            for (int p = 0, i = 0; p < 4; ++p) {
-                if (p == T) continue;
-                const int slot = T - (T > p ? 1 : 0);   // where partner p put group T
-                o[c][rb][i++] = reinterpret_cast<const u4_t*>(smem + (cw + 2 * p) * RED_WAVE)[((c * NRB + rb) * 3 + slot) * 64 + lane];
-            }
-    const int j = lane & 31, h = lane >> 5;
-    // all 128 columns in bounds and 16-byte aligned rows (one uniform test): the reduced fp16
-    // tile is staged in LDS as rows and leaves in whole 128-byte lines, 16 bytes per lane,
-    // with the non-temporal hint (C is written once and not read again here); otherwise
-    // each lane stores its own 4 columns (8 bytes, or element-wise at the edge)
-    const bool staged = (ldc & 7) == 0 && col + BN <= n;
-    const bool full = (ldc & 3) == 0 && col + BN <= n;
-    if (staged) barrier_lds();   // the staged rows overwrite the exchange area: all reads done
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
+            for (int sl = 0; sl < 3; ++sl)
+                o[sl] = *reinterpret_cast<const u4_t*>(smem + (((xr * 4 + W) * 3 + sl) * 64 + lane) * 16);
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // (element-wise __uint_as_float: __builtin_bit_cast of an ext-vector element
-                // reads element 0 with this compiler)
-                v[e] = acc[c][rb][4 * T + e] + __uint_as_float(o[c][rb][0][e]) + __uint_as_float(o[c][rb][1][e]) +
-                       __uint_as_float(o[c][rb][2][e]);
-            }
-            const int r = rb * 32 + j;
-            const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
-            const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
-            const int tc = 64 * cw + 32 * c + 8 * T + 4 * h;   // column inside the tile
-            if (staged) {
-                *reinterpret_cast<u2_t*>(smem + r * STAGE_ROW + 2 * tc) =
-                    u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
-                continue;
-            }
+            for (int e = 0; e < 4; ++e)
+                v[e] = acc[xb][ib][4 * W + e] + __uint_as_float(o[0][e]) + __uint_as_float(o[1][e]) +
+                       __uint_as_float(o[2][e]);
+            const int r = 32 * ib + j;
+            const int cc = 32 * xb + 8 * W + 4 * h;
             if (r >= rows) continue;
             uint16_t* crow = c0 + (long)r * ldc;
-            const int cc = col + tc;
-            if (full) {
+            const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
+            const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
+            if (vec && cc + 4 <= cols) {
                 *reinterpret_cast<u2_t*>(crow + cc) =
                     u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
             } else {
-                if (cc + 0 < n) crow[cc + 0] = h0;
-                if (cc + 1 < n) crow[cc + 1] = h1;
-                if (cc + 2 < n) crow[cc + 2] = h2;
-                if (cc + 3 < n) crow[cc + 3] = h3;
+                if (cc + 0 < cols) crow[cc + 0] = h0;
+                if (cc + 1 < cols) crow[cc + 1] = h1;
+                if (cc + 2 < cols) crow[cc + 2] = h2;
+                if (cc + 3 < cols) crow[cc + 3] = h3;
             }
         }
-    if (staged) {
-        barrier_lds();
-        // 16 lanes per 256-byte tile row, 32 rows per pass of the 512 threads
-        const int tid = threadIdx.x, chunk = tid & 15;
-        for (int r = tid >> 4; r < rows; r += THREADS / 16) {
-            const u4_t val = *reinterpret_cast<const u4_t*>(smem + r * STAGE_ROW + 16 * chunk);
-            __builtin_nontemporal_store(val, reinterpret_cast<u4_t*>(c0 + (long)r * ldc + col + 8 * chunk));
-        }
     }
-}
-
-template <int NRB>
-__device__ __forceinline__ void pk_reduce_store(const f16v_t (&acc)[2][NRB], uint8_t* smem, uint16_t* __restrict__ c0,
-                                                int n, int ldc, int rows, int col, int wave, int lane)
-{
-    switch (wave >> 1) {   // the wave's K quarter (wave-uniform)
-    case 0: pk_reduce_store_q<NRB, 0>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
-    case 1: pk_reduce_store_q<NRB, 1>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
-    case 2: pk_reduce_store_q<NRB, 2>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
-    default: pk_reduce_store_q<NRB, 3>(acc, smem, c0, n, ldc, rows, col, wave, lane); break;
-    }
+    barrier_lds();   // every exchange read is done before the LDS is reused
 }
 
 // ---------------------------------------------------------------------------------------
-// Tile
+// One unit
 // ---------------------------------------------------------------------------------------
 
-// This wave's loads of a tile (see SuperLoads): lane l of a code instruction covers row
-// (first row + l / 8) and stores LDS chunk l % 8, which holds global chunk (l % 8) ^ swz(row).
-template <int SCL>
-__device__ __forceinline__ SuperLoads pk_super_loads(const GroupArgs& G, int n, int k, int row0, int rows, int col0,
-                                                     int rpad, int wave, int lane)
+// Rows [row0, row0 + rows) of group G times columns [col0, col0 + cols), the whole K of the
+// group.  All four waves run the same sequence of loads and barriers.
+template <int NA, int NB>
+__device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, int rows, int col0, int cols,
+                                                   int ldc, bool blocked, uint8_t* smem)
 {
-    using namespace pk;
-    const long qs = k / 2, ss = k / 16;
-    SuperLoads L;
-    const int rl = lane >> 3, pos = lane & 7;
-    L.bb = G.b + (long)col0 * qs;
-    L.ab = G.a + (long)row0 * qs;
+    using Gm = gk::Geo<NA, NB>;
+    constexpr int S = Gm::SLOTS;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nsup = (k + gk::SK - 1) / gk::SK;
+    const int klast = k - gk::SK * (nsup - 1);
+    const auto kt_of = [&](int t) { return t == nsup - 1 ? klast : gk::SK; };
+
+    wait_vm<0>();   // the previous unit's stores are out of the count
+    const UnitLoads<NA, NB> L = unit_loads<NA, NB>(G, k, row0, rows, col0, cols, blocked, wave, lane);
+
+    f16v_t acc[NB][NA];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = wave + 8 * q;   // B code instruction
-        const int r = 8 * i + rl;
-        L.b[q] = (uint32_t)((long)(min(col0 + r, n - 1) - col0) * qs + 16 * (pos ^ swz(r)));
-        L.b_dst[q] = 8 * i * ROWB;
-        L.b_chunk[q] = pos ^ swz(r);
-    }
-    const int na_total = rpad / 8;
-    L.na = 0;
+    for (int x = 0; x < NB; ++x)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int a = ((wave + 4) & 7) + 8 * q;   // A code instruction
-        const int r = 8 * a + rl;
-        L.a[q] = (uint32_t)((long)min(r, rows - 1) * qs + 16 * (pos ^ swz(r)));
-        L.a_dst[q] = A_CODES_AT + 8 * a * ROWB;
-        L.a_chunk[q] = pos ^ swz(r);
-        if (a < na_total) L.na = q + 1;
-    }
-    L.s_dword = lane & 3;
-    if constexpr (SCL == SCL_BLOCKED) {
-        // 128x4 blocked scales: the scale of (row r, K block c) sits in 512-byte atom
-        // (r / 128) * (k / 64) + c / 4 at byte 16 (r % 32) + 4 ((r / 32) % 4) + c % 4, so
-        // the 4 scales of a row in one atom are contiguous.  Lane l of scale instruction
-        // q = wave loads the 4 bytes of row 16 q + l / 4 in the superstep's atom l % 4
-        // (K blocks 16 t + 4 (l % 4) .. +4), which land at LDS byte 16 (row) + 4 (l % 4).
-        // (bases: the tile's first 128-row block; col0 is a multiple of 128, so all B rows
-        // of the tile sit in that block, A rows in it or the next)
-        const long atoms = k / 64;
-        const int piece = lane & 3;
-        const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
-        L.sbb = G.sfb + (long)(col0 >> 7) * atoms * 512;
-        L.nsb = 1;
-        L.sb = (uint32_t)((((long)(gb >> 7) - (col0 >> 7)) * atoms + piece) * 512 + 16 * (gb & 31) +
-                          4 * ((gb >> 5) & 3));
-        L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
-        const int ga = row0 + min(16 * wave + (lane >> 2), rows - 1);
-        L.sab = G.sfa + (long)(row0 >> 7) * atoms * 512;
-        L.nsa = wave < rpad / 16 ? 1 : 0;
-        L.sa = (uint32_t)((((long)(ga >> 7) - (row0 >> 7)) * atoms + piece) * 512 + 16 * (ga & 31) +
-                          4 * ((ga >> 5) & 3));
-        L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
-        L.sstride = 4 * 512;             // four atoms per superstep
-    } else if constexpr (SCL == SCL_ROW4) {
-        // row-major scales, lane l of scale instruction q = wave: dword l % 4 of the
-        // superstep's 16 scale bytes of row 16 q + l / 4
-        const int gb = min(col0 + 16 * wave + (lane >> 2), n - 1);
-        L.sbb = G.sfb + (long)col0 * ss;
-        L.nsb = 1;
-        L.sb = (uint32_t)((long)(gb - col0) * ss + 4 * (lane & 3));
-        L.sb_dst = B_SCALES_AT + 16 * wave * SCB;
-        const int ga = min(16 * wave + (lane >> 2), rows - 1);
-        L.sab = G.sfa + (long)row0 * ss;
-        L.nsa = wave < rpad / 16 ? 1 : 0;
-        L.sa = (uint32_t)((long)ga * ss + 4 * (lane & 3));
-        L.sa_dst = A_CODES_AT + rpad * ROWB + 16 * wave * SCB;
-        L.sstride = SCB;
-    } else {
-        L.sstride = SCB;
-        L.sbb = G.sfb + (long)col0 * ss;
-        L.sab = G.sfa + (long)row0 * ss;
-        L.nsb = wave < 4 ? 1 : 0;        // B scale instruction q = wave
-        L.sb = (uint32_t)((long)(min(col0 + 32 * (wave & 3) + (lane & 31), n - 1) - col0) * ss);
-        L.sb_dst = B_SCALES_AT + 32 * (wave & 3) * SCB;
-        const int qa = 7 - wave;         // A scale instruction
-        L.nsa = qa < rpad / 32 ? 1 : 0;
-        L.sa = (uint32_t)((long)min(32 * qa + (lane & 31), rows - 1) * ss);
-        L.sa_dst = A_CODES_AT + rpad * ROWB + 32 * qa * SCB;
-    }
-    L.ops = 2 + L.nsb + L.na + L.nsa;
-    L.rb = pk_rsrc(L.bb);
-    L.ra = pk_rsrc(L.ab);
-    L.rsb = pk_rsrc(L.sbb);
-    L.rsa = pk_rsrc(L.sab);
-    return L;
-}
+        for (int i = 0; i < NA; ++i) acc[x][i] = f16v_t{};
 
-// ---------------------------------------------------------------------------------------
-// Tile
-// ---------------------------------------------------------------------------------------
-//
-// Every wave reads the raw A bytes of its own K quarter for all tile rows straight from the
-// ring slot, exactly as it reads its B bytes, and dequantises both into MFMA fragments in
-// registers.  The two column halves thus both convert the A rows (a shared fp16 A buffer in
-// LDS would convert them once), which measured cheaper than that buffer's LDS writes,
-// fragment reads and second barrier per superstep; the LDS it would take holds more ring
-// slots instead.
-
-// This lane's LDS byte offsets inside a ring slot: raw codes of half 0 / 1 (column block
-// cb0, row block 0) and the scale words, for B and A.  Both operands use the same lane
-// mapping (lane (j, h), K quarter tq: row j of a 32-row block, chunk 4 half + 2h + tq / 2,
-// bytes 8 (tq % 2) .. +8), and rows 32 apart share the chunk swizzle.
-struct LdsOffs {
-    int ob[2];
-    int oa[2];
-    int obs;
-    int osa;
-};
-
-template <int NRB>
-__device__ __forceinline__ LdsOffs pk_lds_offsets(int lane, int cw, int tq)
-{
-    using namespace pk;
+    // this lane's LDS read offsets inside a slot (wave's K quarter, lane half h, row j)
     const int j = lane & 31, h = lane >> 5;
-    const int brow = 64 * cw + j;
-    LdsOffs o;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int chunk = 4 * half + 2 * h + (tq >> 1);
-        o.ob[half] = brow * ROWB + 16 * (chunk ^ swz(brow)) + 8 * (tq & 1);
-        o.oa[half] = A_CODES_AT + j * ROWB + 16 * (chunk ^ swz(j)) + 8 * (tq & 1);
-    }
-    o.obs = B_SCALES_AT + brow * SCB + 4 * h;
-    o.osa = A_CODES_AT + 32 * NRB * ROWB + j * SCB + 4 * h;
-    return o;
-}
+    const int code_off = j * gk::ROWB + 16 * ((2 * wave + h) ^ gk::swz(j));
+    const int scale_off = (j >> 3) * Gm::SREG + 16 * (j & 7) + 4 * wave + 2 * h;
 
-// Raw bytes of half HALF: 8 code bytes (steps u = 0, 1 in dwords x, y) of B column block c
-// or A row block rb.
-template <int HALF>
-__device__ __forceinline__ u2_t pk_rd_b(const uint8_t* slot, int c, const LdsOffs& o)
-{
-    return *reinterpret_cast<const u2_t*>(slot + o.ob[HALF] + 32 * pk::ROWB * c);
-}
-template <int HALF>
-__device__ __forceinline__ u2_t pk_rd_a(const uint8_t* slot, int rb, const LdsOffs& o)
-{
-    return *reinterpret_cast<const u2_t*>(slot + o.oa[HALF] + 32 * pk::ROWB * rb);
-}
-// The two scale words of a row that the lane needs in a superstep: words h (half 0) and
-// 2 + h (half 1) of the row's 16 scale bytes; byte tq of a word is the lane's scale.
-__device__ __forceinline__ u2_t pk_rd_s(const uint8_t* slot, int off)
-{
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(slot + off);
-    return u2_t{w[0], w[2]};
-}
-
-// Dequantise the raw bytes of half HALF into the MFMA fragments bf[u][c] and af[u][rb].
-template <int NRB, int HALF>
-__device__ __forceinline__ void pk_dequant(h8_t (&bf)[2][2], h8_t (&af)[2][NRB], const u2_t (&qb)[2],
-                                             const u2_t (&qa)[NRB], const u2_t (&srow)[2], const u2_t (&arow)[NRB],
-                                             uint32_t tsel)
-{
-    const h2_t sc = pk_scales<HALF>(srow, tsel);
-    const h2_t s0 = {sc.x, sc.x}, s1 = {sc.y, sc.y};
-    bf[0][0] = __builtin_bit_cast(h8_t, dequant8(qb[0].x, s0));
-    bf[1][0] = __builtin_bit_cast(h8_t, dequant8(qb[0].y, s0));
-    bf[0][1] = __builtin_bit_cast(h8_t, dequant8(qb[1].x, s1));
-    bf[1][1] = __builtin_bit_cast(h8_t, dequant8(qb[1].y, s1));
-#pragma unroll
-    for (int rb = 0; rb < NRB; rb += 2) {
-        const int r1 = rb + 1 < NRB ? rb + 1 : rb;
-        const h2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(arow[r1][HALF], arow[rb][HALF], tsel),
-                                                                 1.0f, false);
-        const h2_t a0 = {sa.x, sa.x};
-        af[0][rb] = __builtin_bit_cast(h8_t, dequant8(qa[rb].x, a0));
-        af[1][rb] = __builtin_bit_cast(h8_t, dequant8(qa[rb].y, a0));
-        if (rb + 1 < NRB) {
-            const h2_t a1 = {sa.y, sa.y};
-            af[0][rb + 1] = __builtin_bit_cast(h8_t, dequant8(qa[rb + 1].x, a1));
-            af[1][rb + 1] = __builtin_bit_cast(h8_t, dequant8(qa[rb + 1].y, a1));
-        }
-    }
-}
-
-// Raw operand bytes of one half superstep in registers: B code bytes of the two column
-// blocks, A code bytes of the row blocks.  Scale words of one superstep: B column blocks,
-// A row blocks.
-template <int NRB>
-struct RawHalf {
-    u2_t b[2];
-    u2_t a[NRB];
-};
-template <int NRB>
-struct ScaleWords {
-    u2_t b[2];
-    u2_t a[NRB];
-};
-
-template <int NRB, int HALF>
-__device__ __forceinline__ void pk_read_raw(RawHalf<NRB>& q, const uint8_t* slot, const LdsOffs& o)
-{
-#pragma unroll
-    for (int c = 0; c < 2; ++c) q.b[c] = pk_rd_b<HALF>(slot, c, o);
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) q.a[rb] = pk_rd_a<HALF>(slot, rb, o);
-}
-
-template <int NRB>
-__device__ __forceinline__ void pk_read_scales(ScaleWords<NRB>& s, const uint8_t* slot, const LdsOffs& o)
-{
-#pragma unroll
-    for (int c = 0; c < 2; ++c) s.b[c] = pk_rd_s(slot, o.obs + 32 * pk::SCB * c);
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) s.a[rb] = pk_rd_s(slot, o.osa + 32 * pk::SCB * rb);
-}
-
-// One half superstep.  The MFMAs consume the fragments bf, af (converted during the
-// previous half); meanwhile the raw bytes q of the next half (read from LDS during the
-// previous half, so their reads have had a whole half to land) are converted into bf, af,
-// and the raw bytes of the half after that are read from `nxt` (the next superstep's slot)
-// into q.  HALF = 0: the next half is half 1 of this superstep (scales s); the half after
-// is half 0 of the next superstep, whose scale words are read too and replace s once this
-// half's conversions are done.  HALF = 1: the next half is half 0 of the next superstep;
-// the half after is its half 1.
-template <int NRB, int HALF>
-__device__ __forceinline__ void pk_half(f16v_t (&acc)[2][NRB], h8_t (&bf)[2][2], h8_t (&af)[2][NRB], RawHalf<NRB>& q,
-                                        ScaleWords<NRB>& s, const uint8_t* nxt, const LdsOffs& o, uint32_t tsel)
-{
-    RawHalf<NRB> qn;
-    ScaleWords<NRB> sn;
-    if constexpr (HALF == 0) {
-        pk_read_scales<NRB>(sn, nxt, o);
-        pk_read_raw<NRB, 0>(qn, nxt, o);
-    } else {
-        pk_read_raw<NRB, 1>(qn, nxt, o);
-    }
-    pk_mfmas<NRB>(acc, bf[0], af[0]);
-    pk_mfmas<NRB>(acc, bf[1], af[1]);
-    pk_dequant<NRB, 1 - HALF>(bf, af, q.b, q.a, s.b, s.a, tsel);
-    q = qn;
-    if constexpr (HALF == 0) s = sn;
-}
-
-// The steady-state load wait of the ring above: AHEAD = slots - 2 supersteps stay in flight.
-template <int NRB, int SCL>
-__device__ __forceinline__ void pk_wait_steady(int n)
-{
-    constexpr bool B4 = SCL != SCL_ROW16;
-    constexpr int AHEAD = pk::ring_slots(32 * NRB) - 2;
-    constexpr int LO = AHEAD * pk_ops_min(NRB, B4), HI = AHEAD * pk_ops_max(NRB, B4);
-    static_assert(HI <= 63, "vmcnt has 6 bits");
-    // s_waitcnt: vmcnt bits 3..0 and 15..14; expcnt (6..4) and lgkmcnt (11..8) not waited for
-    constexpr int EHI = 0x0f70 | (HI & 15) | ((HI >> 4) << 14);
-    constexpr int ELO = 0x0f70 | (LO & 15) | ((LO >> 4) << 14);
-    if (n == HI) {
-        __builtin_amdgcn_s_waitcnt(EHI);
-    } else if (n == LO) {
-        __builtin_amdgcn_s_waitcnt(ELO);
-    } else {
-        pk_wait_loads(n);
-    }
-}
-
-// One full-K tile (rows [row0, row0 + rows) of group G, columns [col0, col0 + 128)), K a
-// multiple of 64 (the last superstep holds k - 256 (supers - 1) K values).  All 8 waves
-// execute the same sequence of loads and barriers; NRB = rpad / 32 sets the MFMAs per B
-// fragment; SCL is how the scales are fetched (ScaleMode).  Raw bytes are read from LDS two
-// halves before their MFMAs and converted one half before.  At the start of superstep t the
-// wave waits for its own loads of superstep t + 1, and the barrier both publishes
-// superstep t + 1 (read during superstep t) and frees slot t (already read during
-// superstep t - 1), which is refilled at once with superstep t + slots.
-template <int NRB, int SCL>
-__device__ __forceinline__ void pk_tile(const GroupArgs& G, int n_, int k_, int row0_, int rows_, int col0_,
-                                        uint8_t* smem)
-{
-    using namespace pk;
-    const int n = __builtin_amdgcn_readfirstlane(n_), k = __builtin_amdgcn_readfirstlane(k_);
-    const int row0 = __builtin_amdgcn_readfirstlane(row0_), rows = __builtin_amdgcn_readfirstlane(rows_);
-    const int col0 = __builtin_amdgcn_readfirstlane(col0_);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cw = wave & 1, tq = wave >> 1;
-    const int rpad = 32 * NRB;
-    const int supers = (k + SK - 1) / SK;
-    const int klast = k - SK * (supers - 1);
-    const int sbytes = slot_bytes(rpad), nslots = ring_slots(rpad);
-    uint8_t* ring = smem;
-    const SuperLoads L = pk_super_loads<SCL>(G, n, k, row0, rows, col0, rpad, wave, lane);
-
-    f16v_t acc[2][NRB];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) acc[c][rb] = f16v_t{};
-
-    // prologue: superstep 0 on its own, then supersteps 1 .. slots-1; convert half 0 of
-    // superstep 0
-    const int first = min(nslots, supers);
-    const auto kt_of = [&](int t) { return t == supers - 1 ? klast : SK; };
-    pk_issue<SCL>(ring, 0, kt_of(0), L, lane);
-    pk_wait_loads(0);
-    for (int t = 1; t < first; ++t) pk_issue<SCL>(ring + t * sbytes, t, kt_of(t), L, lane);
+    const int first = nsup < S ? nsup : S;
+    for (int t = 0; t < first; ++t) issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave, lane);
+    wait_supersteps<Gm::OPS>(first - 1);   // superstep 0 has landed (this wave's part)
     barrier_lds();
-    const uint32_t tsel = 0x0c0c0000u | ((uint32_t)(4 + tq) << 8) | (uint32_t)tq;
-    const LdsOffs lo = pk_lds_offsets<NRB>(lane, cw, tq);
-    // fragments of half 0 of superstep 0, raw bytes of its half 1 and its scale words
-    h8_t bf[2][2], af[2][NRB];
-    RawHalf<NRB> q;
-    ScaleWords<NRB> sw;
-    {
-        RawHalf<NRB> q0;
-        pk_read_scales<NRB>(sw, ring, lo);
-        pk_read_raw<NRB, 0>(q0, ring, lo);
-        pk_read_raw<NRB, 1>(q, ring, lo);
-        pk_dequant<NRB, 0>(bf, af, q0.b, q0.a, sw.b, sw.a, tsel);
-    }
+    RawHalf<NA, NB> h0[2], h1;
+    RawScales<NA, NB> rs[2];
+    Scales<NA, NB> sc[2];
+    Frags<NA, NB> fr[2];
+    read_half<NA, NB, 0>(h0[0], smem, code_off);
+    read_scales<NA, NB>(rs[0], smem, scale_off);
+    convert_scales<NA, NB>(sc[0], rs[0]);
+    convert_step<NA, NB, 0>(fr[0], h0[0], sc[0]);
 
-    const int wait_steady = (nslots - 2) * L.ops;
-    int cs = 0;   // slot of superstep t
-    for (int t = 0; t < supers; ++t) {
-        // superstep t + 1 must have landed (this wave's loads; loads complete in issue
-        // order, so later supersteps stay in flight) before the barrier publishes it; the
-        // barrier also frees slot t, whose bytes are all in registers by now: refill it
-        if (t + nslots - 1 < supers) {
-            pk_wait_steady<NRB, SCL>(wait_steady);   // supersteps t + 2 .. t + slots - 1 in flight
-        } else if (t + 1 < supers) {
-            pk_wait_loads((supers - 2 - t) * L.ops);
-        }
+    // One superstep t (its first half in h0[P], scales in sc[P], step 0's fragments in
+    // fr[0]).  Its second half is read at once; steps 0 and 1 run (MFMAs of a step beside
+    // the next step's conversions).  Then the wave waits for its own loads of superstep
+    // t+1, and the barrier publishes them and frees slot cs (superstep t: both halves have
+    // been read by every wave), which is refilled with superstep t+S; the first half and
+    // the scales of superstep t+1 are read, and steps 2 and 3 run, step 3 beside the
+    // conversion of step 0 of superstep t+1.  In the last superstep the "next" reads and
+    // conversions touch no superstep's bytes: harmless, and their results are unused.
+    int cs = 0;
+    const auto superstep = [&](auto P_, int t) {
+        constexpr int P = decltype(P_)::value;
+        const int ns = cs + 1 == S ? 0 : cs + 1;
+        read_half<NA, NB, 1>(h1, smem + cs * Gm::SLOT, code_off);
+        mfma_step<NA, NB>(acc, fr[0]);
+        convert_step<NA, NB, 1>(fr[1], h0[P], sc[P]);
+        interleave_hint<NA, NB>();
+        mfma_step<NA, NB>(acc, fr[1]);
+        convert_step<NA, NB, 2>(fr[0], h1, sc[P]);
+        interleave_hint<NA, NB>();
+        if (t + 1 < nsup) wait_supersteps<Gm::OPS>(min(S - 2, nsup - 2 - t));
         barrier_lds();
-        if (t + nslots < supers) pk_issue<SCL>(ring + cs * sbytes, t + nslots, kt_of(t + nslots), L, lane);
-        const int ns = (cs + 1 == nslots) ? 0 : cs + 1;
-        // in the last superstep the reads of the "next" slot land on bytes that are no
-        // superstep's: harmless, and their results are unused
-        const uint8_t* nxt = ring + ns * sbytes;
-        pk_half<NRB, 0>(acc, bf, af, q, sw, nxt, lo, tsel);
-        pk_half<NRB, 1>(acc, bf, af, q, sw, nxt, lo, tsel);
+        if (t + S < nsup) issue_superstep<NA, NB>(L, smem + cs * Gm::SLOT, t + S, kt_of(t + S), wave, lane);
+        read_half<NA, NB, 0>(h0[1 - P], smem + ns * Gm::SLOT, code_off);
+        read_scales<NA, NB>(rs[1 - P], smem + ns * Gm::SLOT, scale_off);
+        mfma_step<NA, NB>(acc, fr[0]);
+        convert_step<NA, NB, 3>(fr[1], h1, sc[P]);
+        interleave_hint<NA, NB>();
+        mfma_step<NA, NB>(acc, fr[1]);
+        convert_scales<NA, NB>(sc[1 - P], rs[1 - P]);
+        convert_step<NA, NB, 0>(fr[0], h0[1 - P], sc[1 - P]);
+        interleave_hint<NA, NB>();
         cs = ns;
+    };
+    for (int t = 0; t < nsup; t += 2) {
+        superstep(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < nsup) superstep(std::integral_constant<int, 1>{}, t + 1);
     }
-    // every ring read has completed and every load has landed before the reduction area
-    // overwrites the ring
-    barrier_lds();
-    const int ldc = __builtin_amdgcn_readfirstlane(G.ldc);
-    pk_reduce_store<NRB>(acc, smem, G.c + (long)row0 * ldc, n, ldc, rows, col0, wave, lane);
-    barrier_lds();
+
+    drain_vgpr_acc<NA, NB>(acc);
+    uint16_t* c0 = G.c + (long)row0 * ldc + col0;
+    switch (wave) {
+    case 0: epilogue_w<NA, NB, 0>(acc, smem, c0, rows, cols, ldc, lane); break;
+    case 1: epilogue_w<NA, NB, 1>(acc, smem, c0, rows, cols, ldc, lane); break;
+    case 2: epilogue_w<NA, NB, 2>(acc, smem, c0, rows, cols, ldc, lane); break;
+    default: epilogue_w<NA, NB, 3>(acc, smem, c0, rows, cols, ldc, lane); break;
+    }
 }
 
-// Persistent kernel body: workgroup b processes its first tile tiles[b], then tiles
-// list[begin[b] .. begin[b+1]) in order.
-template <int SCL>
-__device__ __forceinline__ void pk_persistent(uint8_t* smem)
+// ---------------------------------------------------------------------------------------
+// Persistent grouped scheduler
+// ---------------------------------------------------------------------------------------
+
+// Units of group G: ceil(m / 32 na) row chunks times ceil(n / 32 nb) column tiles.
+__device__ __forceinline__ int group_units(const GroupArgs& G)
 {
-    // index the group table in place in the kernarg segment (scalar loads), rather than
-    // through the by-value copy
-    const KernArgs& args = *(const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    const int m = G.m_shape & kMMask;
+    if (m == 0) return 0;
+    const int na = (G.m_shape >> kNaShift) & 15, nb = (G.m_shape >> kNbShift) & 31;
+    return ((m + 32 * na - 1) / (32 * na)) * ((G.n + 32 * nb - 1) / (32 * nb));
+}
+
+// Workgroup b is virtual workgroup v = (b % 8) * vq + b / 8 of V = 8 vq (workgroups are
+// dealt to the 8 XCDs round-robin, so consecutive v share an XCD and its L2); it runs
+// the units [U v / V, U (v+1) / V) of the unit sequence, which lists every group's units
+// in schedule order, row chunks fastest (so the units that read one B column tile are
+// consecutive).  This is the prefix-sum tile enumeration of the persistent scheduler on
+// the page "kernelindex submission 503584" (group found by walking the per-group unit
+// counts, tile decoded from the rank inside the group).
+__global__ __launch_bounds__(gk::THREADS) void nvfp4_gg_units(KernArgs args_byval)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t smem[gk::LDS_BYTES];
+    (void)args_byval;
+    const KernArgs& A = *(const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     const int b = blockIdx.x;
-    // the first tile sits at tiles[b], so its fetch does not wait for the range fetch; the
-    // range is read once (the C stores could alias it as far as the compiler knows)
-    const int i_begin = args.wg_begin[b], i_end = args.wg_begin[b + 1];
-    int idx = b, next = i_begin;
-    while (true) {
-        // the tile is workgroup-uniform: keep it in scalar registers so that the group
-        // table is read from the kernel arguments with scalar loads
-        const TileDesc tv = args.tiles[idx];
-        const TileDesc t = {__builtin_amdgcn_readfirstlane(tv.group), __builtin_amdgcn_readfirstlane(tv.row0),
-                            __builtin_amdgcn_readfirstlane(tv.rows), __builtin_amdgcn_readfirstlane(tv.col0)};
-        const GroupArgs& G = args.grp[t.group];
-        const int n = G.n, k = G.k;
-        switch ((t.rows + 31) >> 5) {   // the planner keeps tiles within 0 .. RMAX rows
-        case 1: pk_tile<1, SCL>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 2: pk_tile<2, SCL>(G, n, k, t.row0, t.rows, t.col0, smem); break;
-        case 3: pk_tile<3, SCL>(G, n, k, t.row0, t.rows, t.col0, smem); break;
+    const int vq = A.vq;
+    const long V = 8L * vq, v = (long)(b & 7) * vq + (b >> 3);
+    const long U = A.units;
+    const int u0 = (int)(U * v / V), u1 = (int)(U * (v + 1) / V);
+    const bool blocked = (A.flags & kFlagBlockedScales) != 0;
+    int gi = 0, gbase = 0;
+    for (int u = u0; u < u1; ++u) {
+        int cnt = group_units(A.grp[gi]);
+        while (u >= gbase + cnt && gi + 1 < A.g) {
+            gbase += cnt;
+            ++gi;
+            cnt = group_units(A.grp[gi]);
+        }
+        const GroupArgs& G = A.grp[gi];
+        const int m = G.m_shape & kMMask;
+        const int na = (G.m_shape >> kNaShift) & 15, nb = (G.m_shape >> kNbShift) & 31;
+        const int rch = (m + 32 * na - 1) / (32 * na);
+        const int l = u - gbase;
+        const int rc = l % rch, ct = l / rch;
+        const int row0 = rc * 32 * na, col0 = ct * 32 * nb;
+        const int rows = min(32 * na, m - row0), cols = min(32 * nb, G.n - col0);
+        switch ((na << 8) | nb) {
+#define NVFP4GG_CASE(NA_, NB_) \
+    case ((NA_) << 8) | (NB_): run_unit<NA_, NB_>(G, G.k, row0, rows, col0, cols, G.ldc, blocked, smem); break;
+            NVFP4GG_UNIT_SHAPES(NVFP4GG_CASE)
+#undef NVFP4GG_CASE
         default: break;
         }
-        if (next >= i_end) break;
-        idx = next++;
     }
 }
 
-// Row-major scales ([rows][k/16]), every k a multiple of 256.
-__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent(KernArgs args_byval)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
-    (void)args_byval;
-    pk_persistent<SCL_ROW16>(smem);
-}
-
-// 128x4 blocked scales (512-byte atoms), k a multiple of 64.
-__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent_blocked(KernArgs args_byval)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
-    (void)args_byval;
-    pk_persistent<SCL_BLOCKED>(smem);
-}
-
-// Row-major scales with some k not a multiple of 256 (scale rows only 4-byte aligned).
-__global__ __launch_bounds__(pk::THREADS) void nvfp4_gg_persistent_ktail(KernArgs args_byval)
-{
-    __shared__ __attribute__((aligned(16))) uint8_t smem[pk::LDS_BYTES];
-    (void)args_byval;
-    pk_persistent<SCL_ROW4>(smem);
-}
-
-VariantShape variant_shape(int variant)
-{
-    switch (variant) {
-    case kVariantPersistent:
-    case kVariantPersistentBlocked:
-    case kVariantPersistentKTail:
-        return VariantShape{pk::RMAX, pk::BN, pk::THREADS, pk::LDS_BYTES};
-    default:
-        return VariantShape{0, 0, 0, 0};
-    }
-}
-
-hipError_t launch_variant(int variant, const KernArgs& args, int grid, hipStream_t stream)
+hipError_t launch_units(const KernArgs& args, int grid, hipStream_t stream)
 {
     if (grid <= 0) return hipSuccess;
     KernArgs a = args;
     void* params[] = {&a};
-    switch (variant) {
-    case kVariantPersistent:
-        return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent), dim3(grid), dim3(pk::THREADS),
-                               params, 0, stream);
-    case kVariantPersistentBlocked:
-        return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent_blocked), dim3(grid),
-                               dim3(pk::THREADS), params, 0, stream);
-    case kVariantPersistentKTail:
-        return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_persistent_ktail), dim3(grid),
-                               dim3(pk::THREADS), params, 0, stream);
-    default:
-        return hipErrorInvalidValue;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&nvfp4_gg_units), dim3(grid), dim3(gk::THREADS), params, 0,
+                           stream);
+}
+
+bool unit_shape_supported(int na, int nb)
+{
+    switch ((na << 8) | nb) {
+#define NVFP4GG_CASE(NA_, NB_) \
+    case ((NA_) << 8) | (NB_): return true;
+        NVFP4GG_UNIT_SHAPES(NVFP4GG_CASE)
+#undef NVFP4GG_CASE
+    default: return false;
+    }
+}
+
+int unit_shape_slots(int na, int nb)
+{
+    switch ((na << 8) | nb) {
+#define NVFP4GG_CASE(NA_, NB_) \
+    case ((NA_) << 8) | (NB_): return gk::Geo<NA_, NB_>::SLOTS;
+        NVFP4GG_UNIT_SHAPES(NVFP4GG_CASE)
+#undef NVFP4GG_CASE
+    default: return 0;
     }
 }
 

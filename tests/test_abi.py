@@ -71,8 +71,8 @@ def ceil_div(a, b):
 @pytest.mark.parametrize("m,n,k", [
     ([80, 176, 128, 72, 64, 248, 96, 160], 4096, 7168),
     ([40, 76, 168, 72, 164, 148, 196, 160], 7168, 2048),
-    ([128, 384], 4096, 1536), ([0, 5, 0, 300], 200, 256), ([64] * 64, 256, 512)])
-def test_host_plan_order_and_tile_prefix(m, n, k):
+    ([128, 384], 4096, 1536), ([0, 5, 0, 300], 200, 256), ([64] * 64, 256, 512), ([8192], 4096, 4096)])
+def test_host_plan_order_and_unit_prefix(m, n, k):
     plan = gg.nvfp4_gg_plan(m, n, k, device=gg.DEVICE_NONE)
     info = gg.nvfp4_gg_plan_info(plan)
     g = len(m)
@@ -81,14 +81,36 @@ def test_host_plan_order_and_tile_prefix(m, n, k):
     assert sorted(order) == list(range(g))
     # largest group first, ties keep the caller order
     assert order == sorted(range(g), key=lambda i: (-m[i], i))
-    tiles = [ceil_div(m[i], info.tile_m) * ceil_div(n, info.tile_n) for i in order]
+    # each group's units: row chunks of unit_rows times column tiles of unit_cols
+    units = []
+    for s in range(g):
+        mi, ur, uc = m[order[s]], info.unit_rows[s], info.unit_cols[s]
+        if mi == 0:
+            assert ur == 0 and uc == 0
+            units.append(0)
+            continue
+        assert ur % 32 == 0 and uc % 32 == 0 and (ur // 32) * (uc // 32) <= 20
+        units.append(ceil_div(mi, ur) * ceil_div(n, uc))
     prefix = [0]
-    for t in tiles:
+    for t in units:
         prefix.append(prefix[-1] + t)
     assert list(info.tile_begin)[:g + 1] == prefix
     assert info.total_tiles == prefix[-1]
-    assert info.grid >= 1 if prefix[-1] else info.grid == 0
-    assert info.block % 64 == 0 and 0 < info.lds_bytes <= 160 * 1024
+    # grid: 8 XCDs x virtual workgroups per XCD, one unit range per workgroup
+    assert info.grid % 8 == 0 and info.grid <= 256
+    assert info.grid >= min(prefix[-1], 256) and info.grid < min(prefix[-1], 256) + 8
+    assert (info.block, info.lds_bytes) == (256, 160 * 1024)
+    assert info.tile_m == max(info.unit_rows[s] for s in range(g))
+    assert info.est_us > 0
+
+
+def test_page_shapes_plan_to_one_unit_range_per_workgroup():
+    # c4 needs 17 accumulator blocks per CU on average; units of up to 20 blocks give every
+    # workgroup at most one unit, and c1/c2 fill every workgroup they use with one unit
+    for m, n, k, most in (([80, 176, 128, 72, 64, 248, 96, 160], 4096, 7168, 1), ([128, 384], 4096, 1536, 1),
+                          ([192, 320], 3072, 4096, 1)):
+        info = gg.nvfp4_gg_plan_info(gg.nvfp4_gg_plan(m, n, k, device=gg.DEVICE_NONE))
+        assert ceil_div(info.total_tiles, info.grid) <= most, (m, info.total_tiles, info.grid)
 
 
 def test_run_validates_pointers_before_touching_the_device():
@@ -132,7 +154,7 @@ def test_plan_layout_validation_and_info():
         plan = gg.nvfp4_gg_plan([100, 3], 64, 256, device=gg.DEVICE_NONE, scale_layout=layout)
         info = gg.nvfp4_gg_plan_info(plan)
         assert info.scale_layout == layout
-        assert info.variant == (3 if layout == gg.SCALES_BLOCKED else 2)
+        assert info.variant == (6 if layout == gg.SCALES_BLOCKED else 5)
         assert info.total_tiles > 0
 
 
@@ -173,24 +195,25 @@ def test_plan_problems_mixed_sizes():
     work = [m * n * k for m, n, k, _ in probs]
     order = [info.order[s] for s in range(4)]
     assert order == sorted(range(4), key=lambda i: -work[i])
-    tiles = [(probs[i][0] + info.tile_m - 1) // info.tile_m * ((probs[i][1] + 127) // 128) if probs[i][0] else 0
-             for i in order]
-    assert [info.tile_begin[s + 1] - info.tile_begin[s] for s in range(4)] == tiles
+    units = [ceil_div(probs[order[s]][0], info.unit_rows[s]) * ceil_div(probs[order[s]][1], info.unit_cols[s])
+             if probs[order[s]][0] else 0 for s in range(4)]
+    assert [info.tile_begin[s + 1] - info.tile_begin[s] for s in range(4)] == units
     # uniform sizes report n and k
     plan2 = gg.nvfp4_gg_plan_problems([(10, 256, 512), (20, 256, 512)], device=gg.DEVICE_NONE)
     info2 = gg.nvfp4_gg_plan_info(plan2)
     assert (info2.n, info2.k) == (256, 512)
 
 
-@pytest.mark.parametrize("k,variant", [(256, 2), (64, 4), (192, 4), (1088, 4), (7168, 2)])
-def test_k_granularity_and_variant(k, variant):
+@pytest.mark.parametrize("k", [256, 64, 192, 1088, 7168])
+def test_k_granularity_and_variant(k):
+    # every multiple of 64 plans (a short last K step); the kernel variant follows the scale
+    # layout only
     plan = gg.nvfp4_gg_plan([100, 7], 96, k, device=gg.DEVICE_NONE)
-    assert gg.nvfp4_gg_plan_info(plan).variant == variant
+    assert gg.nvfp4_gg_plan_info(plan).variant == 5
     blocked = gg.nvfp4_gg_plan([100, 7], 96, k, device=gg.DEVICE_NONE, scale_layout=gg.SCALES_BLOCKED)
-    assert gg.nvfp4_gg_plan_info(blocked).variant == 3
-    # one group with a K tail moves the whole plan to the 4-byte scale variant
+    assert gg.nvfp4_gg_plan_info(blocked).variant == 6
     mixed = gg.nvfp4_gg_plan_problems([(10, 64, 512), (10, 64, k)], device=gg.DEVICE_NONE)
-    assert gg.nvfp4_gg_plan_info(mixed).variant == (2 if k % 256 == 0 else 4)
+    assert gg.nvfp4_gg_plan_info(mixed).total_tiles >= 2
 
 
 def test_build_script_loads_without_the_package():

@@ -1,46 +1,78 @@
-"""GPU parity at the edges of the LDS operand ring.
+"""GPU parity at the edges of the LDS operand ring, for every compiled unit shape.
 
-A tile of 32, 64 or 96 rows streams K through a ring of 7, 5 or 5 superstep slots (K = 256
-each): the first slots are filled up front, and from then on the slot just consumed is
-refilled at the start of every superstep, with a constant load wait in the steady state and a
-shrinking one in the last supersteps.  These cases put the number of supersteps below, at and
-beyond the slot count (several wraps, up to 256 supersteps), with and without a short last
-superstep, for each tile height and both scale layouts (whose load counts per superstep
-differ), plus a very wide n (many tiles per workgroup), and check every element against the
-oracle (same bar and canaries as the per-group tests).  The planner's
-chosen tile height is asserted, so that each case runs the ring it is meant to.
+A unit of NA x NB blocks streams K through a ring of S superstep slots in LDS (K = 256 each;
+S = 3 to 6, by the unit's operand bytes per superstep): the first S supersteps are issued up
+front, and from then on the slot read during the previous superstep is refilled at every
+barrier, with a constant load wait in the steady state and shrinking ones in the last
+supersteps.  For every shape the kernel is compiled for (the planner's choice is overridden
+with NVFP4_GG_FORCE_SHAPE), these cases put the number of supersteps below, at and beyond S
+(several ring wraps), with and without a short last superstep, with ragged rows and columns,
+and check every element against the oracle (same bar and canaries as the per-group tests).
+Units of more than 16 blocks keep their extra accumulators in ordinary VGPRs (a separate code
+path): every such shape runs here too.
 """
+import os
+import re
+
 import pytest
 
 import precision_moe_nvfp4_amd as gg
+from conftest import ROOT
 from test_gpu_parity import say
 from test_gpu_problems import run_problems
 
 pytestmark = pytest.mark.gpu
 
-# (problems, planned chunk height); rows per tile -> 32-row blocks -> ring slots
-CASES = [
-    # 20-row tiles (one 32-row block, 7 slots): 6, 7, 8 and 15 supersteps; 8 with a short last
-    ([(20, 512, 1536, 0), (20, 256, 1792, 0), (20, 256, 2048, 0), (20, 512, 3840, 0), (20, 256, 1856, 0)], 96),
-    # 64-row tiles (5 slots): 6 supersteps, the last one short (64 K values)
-    ([(288, 4096, 1344, 0)], 64),
-    # 90-row tiles (three 32-row blocks, 5 slots): 6 supersteps, the last one short
-    ([(90, 4096, 1344, 0)] * 8, 96),
-    # 90-row tiles: 4, 5 and 11 supersteps
-    ([(90, 4096, 1024, 0)] * 4 + [(90, 4096, 1280, 0)] * 2 + [(90, 4096, 2816, 0)] * 2, 96),
-    # long K: 256 supersteps (36 wraps of a 7-slot ring) and the largest load offsets
-    ([(3, 130, 65536, 0), (3, 64, 65536 - 192, 0)], 96),
-    # wide n: 1024 column tiles over 256 workgroups (4 tiles each), one and 33 rows
-    ([(1, 131072, 256, 0)], 96),
-    ([(33, 131072, 512, 0)], 96),
-]
+
+def compiled_shapes():
+    text = open(os.path.join(ROOT, "precision_moe_nvfp4_amd", "csrc", "nvfp4_gg_internal.h")).read()
+    body = text[text.index("#define NVFP4GG_UNIT_SHAPES(X)"):].split("\n\n", 1)[0]
+    return [(int(a), int(b)) for a, b in re.findall(r"X\((\d+), (\d+)\)", body)]
 
 
-@pytest.mark.parametrize("layout", [gg.SCALES_ROW_MAJOR, gg.SCALES_BLOCKED])
-@pytest.mark.parametrize("case", range(len(CASES)))
-def test_ring_edges(case, layout):
-    problems, chunk = CASES[case]
-    info = gg.nvfp4_gg_plan_info(gg.nvfp4_gg_plan_problems(problems, device=gg.DEVICE_NONE, scale_layout=layout))
-    assert info.tile_m == chunk, f"planned chunk height {info.tile_m}, case expects {chunk}"
-    say(f"ring case {case}: {problems} layout {layout}")
-    run_problems(problems, layout)
+def ring_slots(na, nb):
+    """Slots of the ring for a unit shape (the kernel's geometry: 4 KiB of codes per block and
+    superstep, four scale regions of 128 B per even-rounded block plus 4 B, 160 KiB of LDS)."""
+    nbp, nap = (nb + 1) & ~1, (na + 1) & ~1
+    slot = ((na + nb) * 4096 + 4 * (128 * (nbp + nap) + 4) + 15) & ~15
+    return min(6, (160 * 1024) // slot)
+
+
+SHAPES = compiled_shapes()
+
+
+@pytest.mark.parametrize("na,nb", SHAPES)
+def test_ring_edges_every_shape(na, nb, monkeypatch):
+    S = ring_slots(na, nb)
+    monkeypatch.setenv("NVFP4_GG_FORCE_SHAPE", f"{na},{nb}")
+    # ragged rows (two row chunks, the second short) and columns (last tile short)
+    m1, m2 = 32 * na, max(1, 32 * na - 7)
+    n = 32 * nb + 40
+    cases = [
+        [(m1, n, 256 * (S - 1), 0)],                                   # fewer supersteps than slots
+        [(m2, n, 256 * S + 64, 0)],                                    # S + 1, the last one short
+        [(m1 + m2, n, 256 * (2 * S + 1), 0), (m2, n, 256 * S - 192, 0)],  # wraps; a 64-K tail
+    ]
+    for probs in cases:
+        plan = gg.nvfp4_gg_plan_problems(probs, device=gg.DEVICE_NONE)
+        info = gg.nvfp4_gg_plan_info(plan)
+        assert (info.unit_rows[0], info.unit_cols[0]) == (32 * na, 32 * nb)
+        say(f"ring shape {na}x{nb} (S={S}): {probs}")
+        run_problems(probs, gg.SCALES_ROW_MAJOR)
+
+
+@pytest.mark.parametrize("na,nb", [(4, 4), (4, 5), (2, 9), (1, 1)])
+def test_ring_edges_blocked_scales(na, nb, monkeypatch):
+    S = ring_slots(na, nb)
+    monkeypatch.setenv("NVFP4_GG_FORCE_SHAPE", f"{na},{nb}")
+    probs = [(32 * na + 33, 32 * nb + 40, 256 * (S + 1) + 128, 0), (5, 64, 256 * (S - 1), 0)]
+    say(f"ring shape {na}x{nb} blocked scales: {probs}")
+    run_problems(probs, gg.SCALES_BLOCKED)
+
+
+def test_long_k_and_wide_n():
+    # long K: 256 supersteps (many ring wraps) and the largest load offsets; wide n: many
+    # column tiles per workgroup range
+    for probs in ([(3, 130, 65536, 0), (3, 64, 65536 - 192, 0)], [(1, 131072, 256, 0)], [(33, 131072, 512, 0)]):
+        say(f"ring long/wide: {probs}")
+        run_problems(probs, gg.SCALES_ROW_MAJOR)
