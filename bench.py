@@ -2,22 +2,25 @@
 """Benchmark of the MI355X NVFP4 grouped GEMM (one GPU).
 
 One "step" is one grouped call (nvfp4_gg_run) over one set of synthetic inputs that
-already sit in HBM.  The headline workload is the page's shape g=2, m=[128,384], n=4096,
-k=1536; the other timed page shapes are reported under "shapes" in the same JSON line.
+already sit in HBM.  The headline workload is the largest of the page's timed shapes,
+g=8, m=[80,176,128,72,64,248,96,160], n=4096, k=7168; the other timed shapes are reported
+under "shapes" in the same JSON line, each with its own roofline and CPU-oracle baseline.
 
 Timing protocol (per shape):
   * R input sets rotate so that R * bytes >= 1 GiB (no L2/MALL reuse across calls: "cold");
-  * K calls are captured into one HIP graph (torch.cuda.CUDAGraph) and replayed after W
-    warm-up calls; HIP events on the replay stream bracket the replay; avg per call = t/K;
-  * a second figure re-runs the same K calls as plain launches (host launch overhead
-    included), and a third uses one input set only ("warm");
-  * "us_per_call_spread" gives min / median / max over the headline replay and 4 further
-    replays of the same cold graph.
+    the captured sequence holds max(K, R) calls, so every replay rotates through all R
+    sets whatever K is;
+  * the calls are captured into one HIP graph (torch.cuda.CUDAGraph) and replayed after W
+    warm-up calls and one untimed replay; HIP events on the replay stream bracket each of
+    5 timed replays; per-call time = replay time / calls;
+  * the headline is the median of the 5 replays (min and max reported beside it);
+  * with --full, a direct-launch figure (host launch overhead included) and a one-set
+    ("warm") figure are added.
 The roofline object prices the kernel against the fp16 MFMA dense peak (the path's
 contraction runs on v_mfma_f32_32x32x16_f16) with the algorithmic flops per launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--shapes c1,c2,c3,c4]
-                       [--no-cpu-baseline] [--cold-only] [--calibrate-copy]
+                       [--no-cpu-baseline] [--cold-only] [--full] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -34,15 +37,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "µs per grouped call + achieved HBM TB/s & eff. TFLOP/s (% roofline) per shape"
-HEADLINE = "c1"
+HEADLINE = "c4"
 PAGE_US = {"c1": 10.5, "c2": 14.3, "c3": 45.0, "c4": 47.5}   # B200 timings printed on the page (context)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
 COLD_BYTES = 1 << 30
-SPREAD_REPLAYS = 4             # further timed replays of the cold graph, for min/median/max
+REPLAYS = 5                    # timed replays of the cold graph: median (headline), min, max
 KERNEL_SOURCE = os.path.join(ROOT, "precision_moe_nvfp4_amd", "csrc", "nvfp4_gg_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_gg_c1.md")
-SHAPES_PROFILE = os.path.join(ROOT, "profiles", "kernel_traffic_mfma_nvfp4_gg_c2_c3_c4.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_nvfp4_gg_units.md")
 
 
 DENSE = "8192:4096:4096"
@@ -63,33 +65,26 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; else None."""
+def recorded_shape_traffic():
+    """HBM bytes per launch (read + write, counter-scaled) per shape from the committed
+    rocprofv3 summary, if it was taken on the current kernel source; {} otherwise."""
+    out = {}
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return out
     text = open(TRAFFIC_FILE).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != kernel_source_hash():
-        return None
-    return float(t.group(1))
-
-
-def recorded_shape_traffic():
-    """HBM bytes per launch (read + write, counter-scaled) per page shape from the committed
-    rocprofv3 summaries, if they were taken on the current kernel source; {} otherwise."""
-    out = {}
-    t = recorded_traffic()
-    if t is not None:
-        out[HEADLINE] = t
-    if os.path.exists(SHAPES_PROFILE):
-        text = open(SHAPES_PROFILE).read()
-        h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-        if h and h.group(1) == kernel_source_hash():
-            for m in re.finditer(r"^\| (c\d) \|[^|]*\|[^|]*\| ([0-9,]+) \| ([0-9,]+) \|", text, re.M):
-                out[m.group(1)] = float(m.group(2).replace(",", "")) + float(m.group(3).replace(",", ""))
+    if not h or h.group(1) != kernel_source_hash():
+        return out
+    for m in re.finditer(r"^\| (\S+) \|[^|]*\| ([0-9,]+) \| ([0-9,]+) \|", text, re.M):
+        out[m.group(1)] = float(m.group(2).replace(",", "")) + float(m.group(3).replace(",", ""))
     return out
+
+
+def cold_sequence(steps, nbytes):
+    """Input-set indices of one timed replay: R sets with R * nbytes >= 1 GiB, each call the
+    next set, max(steps, R) calls so that every replay touches all R sets."""
+    R = max(1, math.ceil(COLD_BYTES / nbytes))
+    return [i % R for i in range(max(steps, R))], R
 
 
 def shape_of(name):
@@ -133,11 +128,11 @@ def to_blocked(torch, gg, scales, k, dev):
     return out
 
 
-def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=False):
+def time_shape(torch, gg, name, steps, warmup, dev, full=False, blocked=False):
     cfg = shape_of(name)
     nbytes = algorithmic_bytes(cfg.m, cfg.n, cfg.k)
     flops = algorithmic_flops(cfg.m, cfg.n, cfg.k)
-    R = max(1, math.ceil(COLD_BYTES / nbytes))
+    cold_seq, R = cold_sequence(steps, nbytes)
     cfg, sets, Cs = make_sets(torch, gg, name, R, dev)
     if blocked:
         # the same scale values in the 128x4 blocked layout (converted before timing)
@@ -155,23 +150,21 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
         for r in seq:
             gg.nvfp4_gg_run(plan, args=args[r], stream=h)
 
-    cold_seq = [i % R for i in range(steps)]
-    warm_seq = [0] * steps
     with torch.cuda.stream(stream):
         launches([i % R for i in range(warmup)])
     torch.cuda.synchronize()
 
-    def graph_time(seq, extra=0):
-        """Average per call of one timed replay of the captured sequence; with extra > 0 also
-        the per-call averages of that many further replays (run-to-run spread)."""
+    def graph_times(seq, replays):
+        """Per-call averages of `replays` timed replays of the captured sequence (after one
+        untimed replay)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             launches(seq)
         with torch.cuda.stream(stream):
-            g.replay()   # warm replay
+            g.replay()
         torch.cuda.synchronize()
         times = []
-        for _ in range(1 + extra):
+        for _ in range(replays):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 e0.record(stream)
@@ -179,7 +172,7 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
                 e1.record(stream)
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) * 1000.0 / len(seq))
-        return times if extra else times[0]
+        return sorted(times)
 
     def direct_time(seq):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -191,27 +184,31 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1000.0 / len(seq)
 
-    cold = graph_time(cold_seq, extra=SPREAD_REPLAYS)
-    us_cold = cold[0]   # the headline: exactly one timed replay of the K calls
-    spread = sorted(cold)
-    us_direct = None if cold_only else direct_time(cold_seq)
-    us_warm = None if cold_only else graph_time(warm_seq)
+    cold = graph_times(cold_seq, REPLAYS)
+    us = cold[len(cold) // 2]   # the headline: median of the timed replays
+    us_direct = direct_time(cold_seq) if full else None
+    us_warm = graph_times([0] * max(steps, 1), 3)[1] if full else None
     t_roof_us = max(nbytes / (PEAK_HBM_GBS * 1e3), flops / (PEAK_F16_TFLOPS * 1e6))
+    achieved = flops / us / 1e6
     res = {
-        "us_per_call": round(us_cold, 3),
+        "us_per_call": round(us, 3),
+        "us_per_call_spread": {"min": round(cold[0], 3), "median": round(us, 3), "max": round(cold[-1], 3),
+                               "replays": len(cold)},
         "us_per_call_direct_launch": None if us_direct is None else round(us_direct, 3),
         "us_per_call_warm": None if us_warm is None else round(us_warm, 3),
-        "us_per_call_spread": {"min": round(spread[0], 3), "median": round(spread[len(spread) // 2], 3),
-                               "max": round(spread[-1], 3), "replays": len(spread)},
-        "eff_tflops": round(flops / us_cold / 1e6, 1),
-        "eff_hbm_tbs": round(nbytes / us_cold / 1e6, 3),
+        "eff_tflops": round(achieved, 1),
+        "eff_hbm_tbs": round(nbytes / us / 1e6, 3),
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": flops,
         "roofline_us_f16": round(t_roof_us, 3),
-        "pct_roofline": round(100.0 * t_roof_us / us_cold, 1),
-        "bound": "mfma" if flops / (PEAK_F16_TFLOPS * 1e6) >= nbytes / (PEAK_HBM_GBS * 1e3) else "hbm",
+        "pct_roofline": round(100.0 * t_roof_us / us, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4)},
+        "calls_per_replay": len(cold_seq),
         "rotating_sets": R,
-        "grid": info.grid, "block": info.block, "tile": [info.tile_m, info.tile_n],
+        "rotated_bytes": R * nbytes,
+        "grid": info.grid, "block": info.block, "units": info.total_tiles,
+        "unit_shapes": sorted({(info.unit_rows[s], info.unit_cols[s]) for s in range(len(cfg.m)) if info.unit_rows[s]}),
         "scale_layout": "blocked128x4" if blocked else "row-major",
         "page_b200_us": PAGE_US.get(name),
     }
@@ -221,21 +218,19 @@ def time_shape(torch, gg, name, steps, warmup, dev, cold_only=False, blocked=Fal
     return res
 
 
-def cpu_baseline(name):
-    """The oracle as it stands, timed on the host cores: whole headline calls, repeated for
-    about 10 s of CPU work (at most 30 s), median per call."""
+def cpu_baseline(name, budget_s=8.0):
+    """The oracle as it stands, timed on the host cores: whole calls of the workload,
+    repeated for about `budget_s` seconds of CPU work (at least one call), median per call."""
     import oracle
-    from synthetic import CONFIGS, make_inputs
-    cfg = CONFIGS[name]
+    cfg = shape_of(name)
+    from synthetic import make_inputs
     inp = make_inputs(cfg.m, cfg.n, cfg.k, cfg.seed)
     times = []
     t_start = time.perf_counter()
-    while (time.perf_counter() - t_start) < 10.0 and len(times) < 1000:
+    while not times or ((time.perf_counter() - t_start) < budget_s and len(times) < 1000):
         t0 = time.perf_counter()
         oracle.grouped_inputs(inp, want_abs=False)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > 30.0:
-            break
     times.sort()
     us = times[len(times) // 2] * 1e6
     return {"value": round(us, 1), "unit": "us", "cores": oracle.max_threads(), "kind": "oracle",
@@ -278,8 +273,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--cold-only", action="store_true",
-                    help="time only the cold graph replays (for profiler runs whose kernel "
-                         "average should match the reported value)")
+                    help="time only the cold graph replays of the listed shapes (no blocked-scale "
+                         "line), e.g. for profiler runs whose kernel average should match the value")
+    ap.add_argument("--full", action="store_true", help="also time direct launches and one warm input set")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: --gpus {a.gpus} is not supported: this NVFP4 grouped GEMM runs on one GPU "
@@ -303,24 +299,28 @@ def main():
     shapes = {}
     for nm in names:
         print(f"bench: timing {nm} {shape_of(nm)}", file=sys.stderr, flush=True)
-        shapes[nm] = time_shape(torch, gg, nm, a.steps, a.warmup, dev, cold_only=a.cold_only)
+        shapes[nm] = time_shape(torch, gg, nm, a.steps, a.warmup, dev, full=a.full)
         print(f"bench: {nm} -> {shapes[nm]}", file=sys.stderr, flush=True)
     if not a.cold_only:
         # the headline workload again with its scales in the 128x4 blocked layout
         nm = HEADLINE + "_blocked_scales"
         print(f"bench: timing {nm}", file=sys.stderr, flush=True)
-        shapes[nm] = time_shape(torch, gg, HEADLINE, a.steps, a.warmup, dev, cold_only=True, blocked=True)
+        shapes[nm] = time_shape(torch, gg, HEADLINE, a.steps, a.warmup, dev, blocked=True)
         shapes[nm]["page_b200_us"] = None
         print(f"bench: {nm} -> {shapes[nm]}", file=sys.stderr, flush=True)
     traffic = recorded_shape_traffic()
     for nm, res in shapes.items():
         tb = traffic.get(nm)
-        res["counter_traffic_bytes"] = tb
+        res["roofline"]["traffic"] = tb
         res["counter_hbm_tbs"] = None if tb is None else round(tb / res["us_per_call"] / 1e6, 3)
+    if not a.no_cpu_baseline:
+        for nm in names:
+            if nm in PAGE_US:
+                print(f"bench: timing the CPU oracle on {nm}", file=sys.stderr, flush=True)
+                shapes[nm]["cpu_baseline"] = cpu_baseline(nm)
     head = shapes[HEADLINE]
     cfg = CONFIGS[HEADLINE]
     us = head["us_per_call"]
-    achieved = head["algorithmic_flops"] / us / 1e6  # TFLOP/s
     line = {
         "metric": METRIC,
         "value": us,
@@ -336,16 +336,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"NVFP4 grouped GEMM g={cfg.g} m={list(cfg.m)} n={cfg.n} k={cfg.k} seed={cfg.seed}",
                    "g": cfg.g, "m": list(cfg.m), "n": cfg.n, "k": cfg.k,
-                   "timing": "cold: rotating input sets >= 1 GiB, K calls in one HIP graph, HIP events"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                     "traffic": recorded_traffic(),
-                     "kernel": "nvfp4gg::nvfp4_gg_persistent", "kernel_source_sha256_16": kernel_source_hash()},
+                   "timing": f"cold: {head['rotating_sets']} rotating input sets ({head['rotated_bytes']} bytes) per "
+                             f"replay of {head['calls_per_replay']} calls in one HIP graph, median of "
+                             f"{head['us_per_call_spread']['replays']} replays, HIP events"},
+        "roofline": dict(head["roofline"], kernel="nvfp4gg::nvfp4_gg_units",
+                         kernel_source_sha256_16=kernel_source_hash()),
         "shapes": shapes,
     }
-    if not a.no_cpu_baseline:
-        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(HEADLINE)
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 

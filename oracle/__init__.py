@@ -32,8 +32,8 @@ _lib = None
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the C oracle with gcc (plain C, -O2, OpenMP).  Returns the .so path."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+    """Compile the C oracle with gcc (plain C, -O3 without fast-math, OpenMP).  Returns the .so path."""
+    cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-o", _LIB + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))

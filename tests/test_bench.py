@@ -21,16 +21,24 @@ def _write(path, text):
 
 def test_shape_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     h = bench.kernel_source_hash()
-    table = ("| shape | sizes | kernel us | HBM read bytes | HBM write bytes | x |\n|---|---|---|---|---|---|\n"
-             "| c2 | g=2 | 26.1 (25.9) | 1,000 | 24 | 1.4x |\n| c4 | g=8 | 97.2 (97.2) | 2,000,000 | 8 | 1.4x |\n")
-    shapes = os.path.join(tmp_path, "shapes.md")
-    c1 = os.path.join(tmp_path, "c1.md")
-    _write(shapes, f"kernel_source_sha256_16: {h}\n\n" + table)
-    _write(c1, f"kernel_source_sha256_16: {h}\ntraffic_bytes_per_launch: 777\n")
-    monkeypatch.setattr(bench, "SHAPES_PROFILE", shapes)
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", c1)
-    assert bench.recorded_shape_traffic() == {"c1": 777.0, "c2": 1024.0, "c4": 2_000_008.0}
+    table = ("| shape | sizes | HBM read bytes | HBM write bytes | x |\n|---|---|---|---|---|\n"
+             "| c2 | g=2 | 1,000 | 24 | 1.4x |\n| c4 | g=8 | 2,000,000 | 8 | 1.4x |\n")
+    path = os.path.join(tmp_path, "traffic.md")
+    _write(path, f"kernel_source_sha256_16: {h}\n\n" + table)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
+    assert bench.recorded_shape_traffic() == {"c2": 1024.0, "c4": 2_000_008.0}
     # a summary taken on another kernel source is not used
-    _write(shapes, "kernel_source_sha256_16: 0000000000000000\n\n" + table)
-    _write(c1, "kernel_source_sha256_16: 0000000000000000\ntraffic_bytes_per_launch: 777\n")
+    _write(path, "kernel_source_sha256_16: 0000000000000000\n\n" + table)
     assert bench.recorded_shape_traffic() == {}
+
+
+def test_cold_sequence_rotates_every_set():
+    # the captured sequence of a replay covers all R sets whatever the step count is
+    for name in ("c1", "c2", "c3", "c4"):
+        cfg = bench.shape_of(name)
+        nbytes = bench.algorithmic_bytes(cfg.m, cfg.n, cfg.k)
+        for steps in (1, 20, 200):
+            seq, R = bench.cold_sequence(steps, nbytes)
+            assert R * nbytes >= bench.COLD_BYTES and (R - 1) * nbytes < bench.COLD_BYTES
+            assert set(seq) == set(range(R)) and len(seq) == max(steps, R)
+            assert all(seq[i + 1] != seq[i] for i in range(len(seq) - 1)) or R == 1
