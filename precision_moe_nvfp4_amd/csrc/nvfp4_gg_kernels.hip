@@ -59,18 +59,18 @@ __device__ __forceinline__ uint16_t f16_bits_rne(float f)
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// 8 E2M1 codes (nibble i = element i, i.e. low nibble = even K) times one fp16 scale ->
-// one MFMA fragment (element 2j in the low half of dword j).  The hardware FP4 -> fp16
-// conversion with scale 1.0 gives the exact E2M1 values; one packed fp16 multiply per
-// pair applies the E4M3 scale exactly.
-__device__ __forceinline__ h8_t dequant8(uint32_t x, h2_t s)
+// A fragment dword holds 2 elements: the hardware FP4 -> fp16 conversion of one code byte
+// (low nibble = even K) with scale 1.0 gives the exact E2M1 values, and one packed fp16
+// multiply applies the block's E4M3 scale exactly (convert_dword below).
+
+// Calls f(integral_constant<int, i>) for i = B .. E-1 in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f)
 {
-    u4_t o;
-    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s);
-    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s);
-    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s);
-    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s);
-    return __builtin_bit_cast(h8_t, o);
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -122,13 +122,21 @@ struct Geo {
 // ---------------------------------------------------------------------------------------
 
 // Raw buffer resource over `bytes` bytes at base (at most 2^31 - 1): loads address it as
-// scalar base + 32-bit vector offset + scalar offset, and offsets at or beyond `bytes`
-// read as zero.
+// scalar base + 32-bit vector offset + scalar offset, and vector offsets at or beyond
+// `bytes` read as zero (a direct-to-LDS load then stores zeros).  The base and size are
+// the same in every lane; saying so (readfirstlane) keeps the resource in scalar registers,
+// where a buffer instruction needs it (otherwise every load becomes a loop over lanes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, long bytes)
 {
-    const int n = bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
+    const int n = __builtin_amdgcn_readfirstlane(bytes >= 0x7fffffffL ? 0x7fffffff : (int)bytes);
+    const uint64_t p = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
 }
+
+// A vector offset beyond every buffer range (all ranges are below 2^31 bytes).
+constexpr uint32_t kOffNone = 0x80000000u;
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, uint8_t* lds)
 {
@@ -158,44 +166,41 @@ struct UnitLoads {
 
 // Issue wave w's loads of superstep t (kt = K values it holds: 256 except maybe in the
 // last) into `slot`.  In a short superstep, lanes whose 16-byte code chunk or 4-byte scale
-// word lies beyond K store zeros to their LDS place instead of loading (zero codes and
-// zero scales add exact zeros); every instruction keeps loading lanes, so the number of
-// loads per superstep, and with it every wait count, is the same in all supersteps.
+// word lies beyond K load from an offset outside the buffer, which stores zeros to their
+// LDS place (zero codes and zero scales add exact zeros).  The code is the same for every
+// superstep (no branch), so every wait count is the same in all supersteps too.
 template <int NA, int NB>
-__device__ __forceinline__ void issue_superstep(const UnitLoads<NA, NB>& L, uint8_t* slot, int t, int kt, int wave,
-                                                int lane)
+struct Refill {
+    uint8_t* slot;   // this wave's slot base
+    int soff, ssoff; // code and scale offsets of the superstep
+    bool cv, sv;     // this lane's code chunk / scale word lies inside K
+};
+
+template <int NA, int NB>
+__device__ __forceinline__ Refill<NA, NB> refill_of(const UnitLoads<NA, NB>& L, uint8_t* slot, int t, int kt)
+{
+    return Refill<NA, NB>{slot, t * gk::ROWB, t * L.scl_step, L.code_chunk < (kt >> 5), L.scl_word < (kt >> 6)};
+}
+
+// Load OP of a superstep: B code blocks 0..NB-1, A code blocks, then the scale pairs.
+template <int NA, int NB, int OP>
+__device__ __forceinline__ void issue_op(const UnitLoads<NA, NB>& L, const Refill<NA, NB>& R, int wave)
 {
     using G = gk::Geo<NA, NB>;
-    const int soff = t * gk::ROWB;
-    const int ssoff = t * L.scl_step;
-    if (kt == gk::SK) {
-#pragma unroll
-        for (int x = 0; x < NB; ++x) dma16(L.rb, L.code[x], soff, slot + x * gk::BLK_CODE + wave * 1024);
-#pragma unroll
-        for (int x = 0; x < NA; ++x) dma16(L.ra, L.code[x], soff, slot + (NB + x) * gk::BLK_CODE + wave * 1024);
-#pragma unroll
-        for (int p = 0; p < G::NSI; ++p)
-            dma4(p < G::NBP / 2 ? L.rsb : L.rsa, L.scl[p], ssoff, slot + G::SCALE_AT + wave * G::SREG + p * 256);
-    } else {
-        const bool cv = L.code_chunk < (kt >> 5);
-        const bool sv = L.scl_word < (kt >> 6);
-#pragma unroll
-        for (int x = 0; x < G::NBLK; ++x) {
-            uint8_t* dst = slot + x * gk::BLK_CODE + wave * 1024;
-            if (cv)
-                dma16(x < NB ? L.rb : L.ra, L.code[x < NB ? x : x - NB], soff, dst);
-            else
-                *reinterpret_cast<u4_t*>(dst + 16 * lane) = u4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int p = 0; p < G::NSI; ++p) {
-            uint8_t* dst = slot + G::SCALE_AT + wave * G::SREG + p * 256;
-            if (sv)
-                dma4(p < G::NBP / 2 ? L.rsb : L.rsa, L.scl[p], ssoff, dst);
-            else
-                *reinterpret_cast<uint32_t*>(dst + 4 * lane) = 0u;
-        }
-    }
+    if constexpr (OP < NB)
+        dma16(L.rb, R.cv ? L.code[OP] : kOffNone, R.soff, R.slot + OP * gk::BLK_CODE + wave * 1024);
+    else if constexpr (OP < G::NBLK)
+        dma16(L.ra, R.cv ? L.code[OP - NB] : kOffNone, R.soff, R.slot + OP * gk::BLK_CODE + wave * 1024);
+    else
+        dma4(OP - G::NBLK < G::NBP / 2 ? L.rsb : L.rsa, R.sv ? L.scl[OP - G::NBLK] : kOffNone, R.ssoff,
+             R.slot + G::SCALE_AT + wave * G::SREG + (OP - G::NBLK) * 256);
+}
+
+template <int NA, int NB>
+__device__ __forceinline__ void issue_superstep(const UnitLoads<NA, NB>& L, uint8_t* slot, int t, int kt, int wave)
+{
+    const Refill<NA, NB> R = refill_of<NA, NB>(L, slot, t, kt);
+    static_for<0, gk::Geo<NA, NB>::OPS>([&](auto op) { issue_op<NA, NB, decltype(op)::value>(L, R, wave); });
 }
 
 // Per-lane load offsets and buffer resources of one unit (see UnitLoads).  `rows` / `cols`
@@ -260,19 +265,6 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// Wait until at most n * OPS of this wave's loads are in flight (0 <= n <= 4).
-template <int OPS>
-__device__ __forceinline__ void wait_supersteps(int n)
-{
-    switch (n) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<(OPS <= 63 ? OPS : 63)>(); break;
-    case 2: wait_vm<(2 * OPS <= 63 ? 2 * OPS : 63)>(); break;
-    case 3: wait_vm<(3 * OPS <= 63 ? 3 * OPS : 63)>(); break;
-    default: wait_vm<(4 * OPS <= 63 ? 4 * OPS : 63)>(); break;
-    }
-}
-
 // Workgroup barrier for LDS hand-offs: waits for this wave's own LDS reads and writes, then
 // s_barrier.  Unlike __syncthreads() it does not wait for outstanding direct-to-LDS loads
 // (those are waited for explicitly, so later supersteps stay in flight).
@@ -323,10 +315,11 @@ __device__ __forceinline__ void read_scales(RawScales<NA, NB>& R, const uint8_t*
         R.sa[i] = *reinterpret_cast<const uint16_t*>(slot + Gm::SCALE_AT + scale_off + 128 * (Gm::NBP + i));
 }
 
-// MFMA fragments of one 16-K step: one per B block and one per A block.
+// MFMA fragments of one 16-K step: one per B block and one per A block (dword e holds
+// elements 2e and 2e + 1 as fp16).
 template <int NA, int NB>
 struct Frags {
-    h8_t b[NB], a[NA];
+    u4_t b[NB], a[NA];
 };
 
 // The fp16 scale pairs of a superstep (element 0: steps 0 and 1, element 1: steps 2 and 3).
@@ -335,29 +328,46 @@ struct Scales {
     h2_t b[NB], a[NA];
 };
 
+// Scale pair of block Y (B blocks first, then A blocks) from its two raw E4M3 bytes.
+template <int NA, int NB, int Y>
+__device__ __forceinline__ void convert_scale(Scales<NA, NB>& S, const RawScales<NA, NB>& R)
+{
+    if constexpr (Y < NB)
+        S.b[Y] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.sb[Y], 1.0f, false);
+    else
+        S.a[Y - NB] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.sa[Y - NB], 1.0f, false);
+}
+
+// Dword E of fragment Y (B blocks first, then A blocks) of step ST (0..3) of a superstep,
+// from the half that holds it: two E2M1 codes (byte E of the step's code dword) converted
+// exactly by the hardware, times the block's E4M3 scale in fp16 (exact, see above).
+template <int NA, int NB, int ST, int Y, int E>
+__device__ __forceinline__ void convert_dword(Frags<NA, NB>& F, const RawHalf<NA, NB>& R, const Scales<NA, NB>& S)
+{
+    if constexpr (Y < NB) {
+        const _Float16 c = ST < 2 ? S.b[Y].x : S.b[Y].y;
+        F.b[Y][E] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(R.cb[Y][ST & 1], 1.0f, E) * h2_t{c, c});
+    } else {
+        const _Float16 c = ST < 2 ? S.a[Y - NB].x : S.a[Y - NB].y;
+        F.a[Y - NB][E] = __builtin_bit_cast(
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(R.ca[Y - NB][ST & 1], 1.0f, E) * h2_t{c, c});
+    }
+}
+
 template <int NA, int NB>
 __device__ __forceinline__ void convert_scales(Scales<NA, NB>& S, const RawScales<NA, NB>& R)
 {
-#pragma unroll
-    for (int x = 0; x < NB; ++x) S.b[x] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.sb[x], 1.0f, false);
-#pragma unroll
-    for (int i = 0; i < NA; ++i) S.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.sa[i], 1.0f, false);
+    static_for<0, NA + NB>([&](auto y) { convert_scale<NA, NB, decltype(y)::value>(S, R); });
 }
 
-// Fragments of step ST (0..3) of a superstep from the half that holds it.
 template <int NA, int NB, int ST>
 __device__ __forceinline__ void convert_step(Frags<NA, NB>& F, const RawHalf<NA, NB>& R, const Scales<NA, NB>& S)
 {
-#pragma unroll
-    for (int x = 0; x < NB; ++x) {
-        const _Float16 c = ST < 2 ? S.b[x].x : S.b[x].y;
-        F.b[x] = dequant8(R.cb[x][ST & 1], h2_t{c, c});
-    }
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-        const _Float16 c = ST < 2 ? S.a[i].x : S.a[i].y;
-        F.a[i] = dequant8(R.ca[i][ST & 1], h2_t{c, c});
-    }
+    static_for<0, 4 * (NA + NB)>([&](auto j) {
+        constexpr int J = decltype(j)::value;
+        convert_dword<NA, NB, ST, J / 4, J % 4>(F, R, S);
+    });
 }
 
 // Accumulator blocks 0..15 (x * NA + i) live in the 256 accumulation registers; a unit with
@@ -368,23 +378,37 @@ __device__ __forceinline__ void convert_step(Frags<NA, NB>& F, const RawHalf<NA,
 // the reads of its source fragments by the VALU that may overwrite them next.
 constexpr int kAgprBlocks = 16;
 
-__device__ __forceinline__ void mfma_vgpr_acc(f16v_t& acc, const h8_t& b, const h8_t& a)
+__device__ __forceinline__ void mfma_vgpr_acc(f16v_t& acc, const u4_t& b, const u4_t& a)
 {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 1" : "+v"(acc) : "v"(b), "v"(a));
 }
 
-template <int NA, int NB>
-__device__ __forceinline__ void mfma_step(f16v_t (&acc)[NB][NA], const Frags<NA, NB>& F)
+// MFMA of accumulator block Q (column block Q / NA, row block Q % NA).
+template <int NA, int NB, int Q>
+__device__ __forceinline__ void mfma_block(f16v_t (&acc)[NB][NA], const Frags<NA, NB>& F)
 {
-#pragma unroll
-    for (int x = 0; x < NB; ++x)
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            if (x * NA + i < kAgprBlocks)
-                acc[x][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.b[x], F.a[i], acc[x][i], 0, 0, 0);
-            else
-                mfma_vgpr_acc(acc[x][i], F.b[x], F.a[i]);
-        }
+    constexpr int x = Q / NA, i = Q % NA;
+    if constexpr (Q < kAgprBlocks)
+        acc[x][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, F.b[x]),
+                                                         __builtin_bit_cast(h8_t, F.a[i]), acc[x][i], 0, 0, 0);
+    else
+        mfma_vgpr_acc(acc[x][i], F.b[x], F.a[i]);
+}
+
+// One 16-K step in program order: the NA * NB MFMAs, each followed by its share of the NL
+// loads and the NJ VALU jobs that prepare the next step, fenced so that the compiler keeps
+// this order (a VALU job issues while the MFMA before it runs; loads reach the memory
+// pipeline spread over the step).
+template <int NM, int NJ, int NL, class M, class J, class L>
+__device__ __forceinline__ void bundled_step(M&& mfma, J&& job, L&& load)
+{
+    static_for<0, NM>([&](auto q) {
+        constexpr int Q = decltype(q)::value;
+        mfma(q);
+        static_for<Q * NL / NM, (Q + 1) * NL / NM>(load);
+        static_for<Q * NJ / NM, (Q + 1) * NJ / NM>(job);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // After the last MFMA of a unit: the written-out MFMAs' results become readable by the VALU
@@ -408,21 +432,6 @@ __device__ __forceinline__ void drain_vgpr_acc(f16v_t (&acc)[NB][NA])
     }
 }
 
-// Ask the scheduler to interleave the step's MFMAs with the next step's conversions: one
-// MFMA, then about as many VALU instructions as hide behind it.
-template <int NA, int NB>
-__device__ __forceinline__ void interleave_hint()
-{
-    constexpr int NM = NA * NB;
-    constexpr int NV = 8 * (NA + NB);
-    constexpr int PER = (NV + NM - 1) / NM;
-#pragma unroll
-    for (int q = 0; q < NM; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);   // then VALU
-    }
-}
-
 // ---------------------------------------------------------------------------------------
 // Epilogue
 // ---------------------------------------------------------------------------------------
@@ -440,51 +449,63 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
     constexpr int RR = Gm::RED_ROUND;
     const int j = lane & 31, h = lane >> 5;
     const bool vec = (ldc & 3) == 0;
-#pragma unroll
-    for (int r0 = 0; r0 < Gm::NACC; r0 += RR) {
+    // exchange place of element group q's copy from partner slot sl, round block xr
+    const auto at = [&](int xr, int q, int sl) { return smem + (((xr * 4 + q) * 3 + sl) * 64 + lane) * 16; };
+    static_for<0, (Gm::NACC + RR - 1) / RR>([&](auto rd) {
+        constexpr int R0 = decltype(rd)::value * RR;
+        constexpr int NR = Gm::NACC - R0 < RR ? Gm::NACC - R0 : RR;
         barrier_lds();   // the ring, or the previous round's exchange, is no longer read
-#pragma unroll
-        for (int xr = 0; xr < RR && r0 + xr < Gm::NACC; ++xr) {
-            const int xb = (r0 + xr) / NA, ib = (r0 + xr) % NA;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q == W) continue;
-                const int slot = W - (W > q ? 1 : 0);
-                *reinterpret_cast<u4_t*>(smem + (((xr * 4 + q) * 3 + slot) * 64 + lane) * 16) =
-                    u4_t{__float_as_uint(acc[xb][ib][4 * q + 0]), __float_as_uint(acc[xb][ib][4 * q + 1]),
-                         __float_as_uint(acc[xb][ib][4 * q + 2]), __float_as_uint(acc[xb][ib][4 * q + 3])};
-            }
-        }
+        static_for<0, NR>([&](auto xr_) {
+            constexpr int XR = decltype(xr_)::value;
+            constexpr int xb = (R0 + XR) / NA, ib = (R0 + XR) % NA;
+            static_for<0, 4>([&](auto q_) {
+                constexpr int Q = decltype(q_)::value;
+                if constexpr (Q != W) {
+                    constexpr int SL = W - (W > Q ? 1 : 0);
+                    *reinterpret_cast<u4_t*>(at(XR, Q, SL)) =
+                        u4_t{__float_as_uint(acc[xb][ib][4 * Q + 0]), __float_as_uint(acc[xb][ib][4 * Q + 1]),
+                             __float_as_uint(acc[xb][ib][4 * Q + 2]), __float_as_uint(acc[xb][ib][4 * Q + 3])};
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);   // one block's copies at a time (register pressure)
+        });
         barrier_lds();
-#pragma unroll
-        for (int xr = 0; xr < RR && r0 + xr < Gm::NACC; ++xr) {
-            const int xb = (r0 + xr) / NA, ib = (r0 + xr) % NA;
-            u4_t o[3];
-#pragma unroll
-            for (int sl = 0; sl < 3; ++sl)
-                o[sl] = *reinterpret_cast<const u4_t*>(smem + (((xr * 4 + W) * 3 + sl) * 64 + lane) * 16);
+        // read the partner copies one block ahead of the sums that use them
+        u4_t o[2][3];
+        static_for<0, 3>([&](auto sl) { o[0][decltype(sl)::value] = *reinterpret_cast<const u4_t*>(at(0, W, sl)); });
+        static_for<0, NR>([&](auto xr_) {
+            constexpr int XR = decltype(xr_)::value;
+            constexpr int xb = (R0 + XR) / NA, ib = (R0 + XR) % NA;
+            if constexpr (XR + 1 < NR)
+                static_for<0, 3>([&](auto sl) {
+                    o[(XR + 1) & 1][decltype(sl)::value] = *reinterpret_cast<const u4_t*>(at(XR + 1, W, sl));
+                });
+            __builtin_amdgcn_sched_barrier(0);
             float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = acc[xb][ib][4 * W + e] + __uint_as_float(o[0][e]) + __uint_as_float(o[1][e]) +
-                       __uint_as_float(o[2][e]);
+            static_for<0, 4>([&](auto e_) {
+                constexpr int E = decltype(e_)::value;
+                v[E] = acc[xb][ib][4 * W + E] + __uint_as_float(o[XR & 1][0][E]) + __uint_as_float(o[XR & 1][1][E]) +
+                       __uint_as_float(o[XR & 1][2][E]);
+            });
             const int r = 32 * ib + j;
             const int cc = 32 * xb + 8 * W + 4 * h;
-            if (r >= rows) continue;
-            uint16_t* crow = c0 + (long)r * ldc;
-            const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
-            const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
-            if (vec && cc + 4 <= cols) {
-                *reinterpret_cast<u2_t*>(crow + cc) =
-                    u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
-            } else {
-                if (cc + 0 < cols) crow[cc + 0] = h0;
-                if (cc + 1 < cols) crow[cc + 1] = h1;
-                if (cc + 2 < cols) crow[cc + 2] = h2;
-                if (cc + 3 < cols) crow[cc + 3] = h3;
+            if (r < rows) {
+                uint16_t* crow = c0 + (long)r * ldc;
+                const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
+                const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
+                if (vec && cc + 4 <= cols) {
+                    *reinterpret_cast<u2_t*>(crow + cc) =
+                        u2_t{(uint32_t)h0 | ((uint32_t)h1 << 16), (uint32_t)h2 | ((uint32_t)h3 << 16)};
+                } else {
+                    if (cc + 0 < cols) crow[cc + 0] = h0;
+                    if (cc + 1 < cols) crow[cc + 1] = h1;
+                    if (cc + 2 < cols) crow[cc + 2] = h2;
+                    if (cc + 3 < cols) crow[cc + 3] = h3;
+                }
             }
-        }
-    }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    });
     barrier_lds();   // every exchange read is done before the LDS is reused
 }
 
@@ -504,7 +525,10 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nsup = (k + gk::SK - 1) / gk::SK;
     const int klast = k - gk::SK * (nsup - 1);
-    const auto kt_of = [&](int t) { return t == nsup - 1 ? klast : gk::SK; };
+    // K values of superstep t: 256, the tail in the last, none beyond (such supersteps are
+    // still "loaded", every lane from outside the buffers, which stores zeros: so every
+    // superstep issues the same loads and waits with the same count)
+    const auto kt_of = [&](int t) { return t < nsup - 1 ? gk::SK : t == nsup - 1 ? klast : 0; };
 
     wait_vm<0>();   // the previous unit's stores are out of the count
     const UnitLoads<NA, NB> L = unit_loads<NA, NB>(G, k, row0, rows, col0, cols, blocked, wave, lane);
@@ -520,9 +544,8 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     const int code_off = j * gk::ROWB + 16 * ((2 * wave + h) ^ gk::swz(j));
     const int scale_off = (j >> 3) * Gm::SREG + 16 * (j & 7) + 4 * wave + 2 * h;
 
-    const int first = nsup < S ? nsup : S;
-    for (int t = 0; t < first; ++t) issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave, lane);
-    wait_supersteps<Gm::OPS>(first - 1);   // superstep 0 has landed (this wave's part)
+    static_for<0, S>([&](auto t) { issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave); });
+    wait_vm<(S - 1) * Gm::OPS>();   // superstep 0 has landed (this wave's part)
     barrier_lds();
     RawHalf<NA, NB> h0[2], h1;
     RawScales<NA, NB> rs[2];
@@ -541,35 +564,60 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     // the scales of superstep t+1 are read, and steps 2 and 3 run, step 3 beside the
     // conversion of step 0 of superstep t+1.  In the last superstep the "next" reads and
     // conversions touch no superstep's bytes: harmless, and their results are unused.
+    // Every superstep refills its slot (with zeros beyond the last superstep) and waits with
+    // the same count; the refill's loads are spread over step 2.
+    constexpr int NM = NA * NB;
+    constexpr int NJ = 4 * Gm::NBLK;   // VALU jobs of one step's conversion
+    const auto no_load = [](auto) {};
     int cs = 0;
     const auto superstep = [&](auto P_, int t) {
         constexpr int P = decltype(P_)::value;
         const int ns = cs + 1 == S ? 0 : cs + 1;
         read_half<NA, NB, 1>(h1, smem + cs * Gm::SLOT, code_off);
-        mfma_step<NA, NB>(acc, fr[0]);
-        convert_step<NA, NB, 1>(fr[1], h0[P], sc[P]);
-        interleave_hint<NA, NB>();
-        mfma_step<NA, NB>(acc, fr[1]);
-        convert_step<NA, NB, 2>(fr[0], h1, sc[P]);
-        interleave_hint<NA, NB>();
-        if (t + 1 < nsup) wait_supersteps<Gm::OPS>(min(S - 2, nsup - 2 - t));
+        __builtin_amdgcn_sched_barrier(0);   // the LDS reads go out first
+        bundled_step<NM, NJ, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[0]); },
+                                [&](auto j) {
+                                    constexpr int J = decltype(j)::value;
+                                    convert_dword<NA, NB, 1, J / 4, J % 4>(fr[1], h0[P], sc[P]);
+                                },
+                                no_load);
+        bundled_step<NM, NJ, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[1]); },
+                                [&](auto j) {
+                                    constexpr int J = decltype(j)::value;
+                                    convert_dword<NA, NB, 2, J / 4, J % 4>(fr[0], h1, sc[P]);
+                                },
+                                no_load);
+        wait_vm<(S - 2) * Gm::OPS>();
         barrier_lds();
-        if (t + S < nsup) issue_superstep<NA, NB>(L, smem + cs * Gm::SLOT, t + S, kt_of(t + S), wave, lane);
         read_half<NA, NB, 0>(h0[1 - P], smem + ns * Gm::SLOT, code_off);
         read_scales<NA, NB>(rs[1 - P], smem + ns * Gm::SLOT, scale_off);
-        mfma_step<NA, NB>(acc, fr[0]);
-        convert_step<NA, NB, 3>(fr[1], h1, sc[P]);
-        interleave_hint<NA, NB>();
-        mfma_step<NA, NB>(acc, fr[1]);
-        convert_scales<NA, NB>(sc[1 - P], rs[1 - P]);
-        convert_step<NA, NB, 0>(fr[0], h0[1 - P], sc[1 - P]);
-        interleave_hint<NA, NB>();
+        __builtin_amdgcn_sched_barrier(0);
+        const auto step2_jobs = [&](auto j) {
+            constexpr int J = decltype(j)::value;
+            convert_dword<NA, NB, 3, J / 4, J % 4>(fr[1], h1, sc[P]);
+        };
+        const auto step2_mfma = [&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[0]); };
+        const Refill<NA, NB> R = refill_of<NA, NB>(L, smem + cs * Gm::SLOT, t + S, kt_of(t + S));
+        bundled_step<NM, NJ, Gm::OPS>(step2_mfma, step2_jobs,
+                                      [&](auto op) { issue_op<NA, NB, decltype(op)::value>(L, R, wave); });
+        // step 3: first the next superstep's scales, then its step 0 fragments
+        bundled_step<NM, NJ + Gm::NBLK, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[1]); },
+                                           [&](auto j) {
+                                               constexpr int J = decltype(j)::value;
+                                               if constexpr (J < Gm::NBLK)
+                                                   convert_scale<NA, NB, J>(sc[1 - P], rs[1 - P]);
+                                               else
+                                                   convert_dword<NA, NB, 0, (J - Gm::NBLK) / 4, (J - Gm::NBLK) % 4>(
+                                                       fr[0], h0[1 - P], sc[1 - P]);
+                                           },
+                                           no_load);
         cs = ns;
     };
     for (int t = 0; t < nsup; t += 2) {
         superstep(std::integral_constant<int, 0>{}, t);
         if (t + 1 < nsup) superstep(std::integral_constant<int, 1>{}, t + 1);
     }
+    wait_vm<0>();   // the zero refills beyond the last superstep have landed before the LDS is reused
 
     drain_vgpr_acc<NA, NB>(acc);
     uint16_t* c0 = G.c + (long)row0 * ldc + col0;
