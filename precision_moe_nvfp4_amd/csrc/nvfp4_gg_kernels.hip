@@ -109,6 +109,10 @@ struct Geo {
     static constexpr int NSI = (NBP + NAP) / 2;    // scale load instructions per wave
     static constexpr int OPS = NBLK + NSI;         // loads per wave and superstep
     static constexpr int NACC = NA * NB;           // accumulator blocks
+    // each lane reads its 16 code bytes of a block in one LDS read per superstep, except in
+    // the units with the most registers in use (20 accumulator blocks, or 11 operand blocks),
+    // which read them in two 8-byte halves (two fewer code registers per block)
+    static constexpr bool FULL_READS = NACC < 20 && NBLK < 11;
     // epilogue exchange: per block, 4 element groups x 3 partner copies x 1 KiB
     static constexpr int RED_BLK = 3 * 4 * 1024;
     static constexpr int RED_ROUND = (LDS_BYTES / RED_BLK) < NACC ? (LDS_BYTES / RED_BLK) : NACC;
@@ -281,10 +285,13 @@ __device__ __forceinline__ void barrier_lds()
 // Compute
 // ---------------------------------------------------------------------------------------
 
-// This wave's raw code bytes of one half superstep (steps 0-1 or 2-3): 8 bytes per block.
-template <int NA, int NB>
-struct RawHalf {
-    u2_t cb[NB], ca[NA];
+// This wave's raw code dwords (one per 16-K step) of a superstep, W = 4: all four steps
+// (one 16-byte read per block), or W = 2: one half of it (steps 0-1 or 2-3, one 8-byte
+// read per block).
+template <int NA, int NB, int W>
+struct RawCodes {
+    using V = std::conditional_t<W == 4, u4_t, u2_t>;
+    V cb[NB], ca[NA];
 };
 
 // The two scale bytes of each block's row in one superstep (low byte: steps 0 and 1, high
@@ -294,14 +301,37 @@ struct RawScales {
     uint32_t sb[NB], sa[NA];
 };
 
-template <int NA, int NB, int H>
-__device__ __forceinline__ void read_half(RawHalf<NA, NB>& R, const uint8_t* slot, int code_off)
+// The code read of block Y (B blocks first, then A blocks).
+template <int NA, int NB, int W, int OFF, int Y>
+__device__ __forceinline__ void read_code(RawCodes<NA, NB, W>& R, const uint8_t* slot, int code_off)
 {
+    using V = typename RawCodes<NA, NB, W>::V;
+    if constexpr (Y < NB)
+        R.cb[Y] = *reinterpret_cast<const V*>(slot + Y * gk::BLK_CODE + code_off + OFF);
+    else
+        R.ca[Y - NB] = *reinterpret_cast<const V*>(slot + Y * gk::BLK_CODE + code_off + OFF);
+}
+
+template <int NA, int NB, int W, int OFF>
+__device__ __forceinline__ void read_codes(RawCodes<NA, NB, W>& R, const uint8_t* slot, int code_off)
+{
+    using V = typename RawCodes<NA, NB, W>::V;
 #pragma unroll
-    for (int x = 0; x < NB; ++x) R.cb[x] = *reinterpret_cast<const u2_t*>(slot + x * gk::BLK_CODE + code_off + 8 * H);
+    for (int x = 0; x < NB; ++x) R.cb[x] = *reinterpret_cast<const V*>(slot + x * gk::BLK_CODE + code_off + OFF);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-        R.ca[i] = *reinterpret_cast<const u2_t*>(slot + (NB + i) * gk::BLK_CODE + code_off + 8 * H);
+        R.ca[i] = *reinterpret_cast<const V*>(slot + (NB + i) * gk::BLK_CODE + code_off + OFF);
+}
+
+// The scale read of block Y (B blocks first, then A blocks).
+template <int NA, int NB, int Y>
+__device__ __forceinline__ void read_scale(RawScales<NA, NB>& R, const uint8_t* slot, int scale_off)
+{
+    using Gm = gk::Geo<NA, NB>;
+    if constexpr (Y < NB)
+        R.sb[Y] = *reinterpret_cast<const uint16_t*>(slot + Gm::SCALE_AT + scale_off + 128 * Y);
+    else
+        R.sa[Y - NB] = *reinterpret_cast<const uint16_t*>(slot + Gm::SCALE_AT + scale_off + 128 * (Gm::NBP + Y - NB));
 }
 
 template <int NA, int NB>
@@ -339,19 +369,20 @@ __device__ __forceinline__ void convert_scale(Scales<NA, NB>& S, const RawScales
 }
 
 // Dword E of fragment Y (B blocks first, then A blocks) of step ST (0..3) of a superstep,
-// from the half that holds it: two E2M1 codes (byte E of the step's code dword) converted
-// exactly by the hardware, times the block's E4M3 scale in fp16 (exact, see above).
-template <int NA, int NB, int ST, int Y, int E>
-__device__ __forceinline__ void convert_dword(Frags<NA, NB>& F, const RawHalf<NA, NB>& R, const Scales<NA, NB>& S)
+// from dword D of the raw codes that hold it: two E2M1 codes (byte E of the step's code
+// dword) converted exactly by the hardware, times the block's E4M3 scale in fp16 (exact,
+// see above).
+template <int NA, int NB, int ST, int D, int Y, int E, int W>
+__device__ __forceinline__ void convert_dword(Frags<NA, NB>& F, const RawCodes<NA, NB, W>& R, const Scales<NA, NB>& S)
 {
     if constexpr (Y < NB) {
         const _Float16 c = ST < 2 ? S.b[Y].x : S.b[Y].y;
-        F.b[Y][E] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(R.cb[Y][ST & 1], 1.0f, E) * h2_t{c, c});
+        F.b[Y][E] = __builtin_bit_cast(uint32_t,
+                                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(R.cb[Y][D], 1.0f, E) * h2_t{c, c});
     } else {
         const _Float16 c = ST < 2 ? S.a[Y - NB].x : S.a[Y - NB].y;
         F.a[Y - NB][E] = __builtin_bit_cast(
-            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(R.ca[Y - NB][ST & 1], 1.0f, E) * h2_t{c, c});
+            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(R.ca[Y - NB][D], 1.0f, E) * h2_t{c, c});
     }
 }
 
@@ -361,12 +392,12 @@ __device__ __forceinline__ void convert_scales(Scales<NA, NB>& S, const RawScale
     static_for<0, NA + NB>([&](auto y) { convert_scale<NA, NB, decltype(y)::value>(S, R); });
 }
 
-template <int NA, int NB, int ST>
-__device__ __forceinline__ void convert_step(Frags<NA, NB>& F, const RawHalf<NA, NB>& R, const Scales<NA, NB>& S)
+template <int NA, int NB, int ST, int D, int W>
+__device__ __forceinline__ void convert_step(Frags<NA, NB>& F, const RawCodes<NA, NB, W>& R, const Scales<NA, NB>& S)
 {
     static_for<0, 4 * (NA + NB)>([&](auto j) {
         constexpr int J = decltype(j)::value;
-        convert_dword<NA, NB, ST, J / 4, J % 4>(F, R, S);
+        convert_dword<NA, NB, ST, D, J / 4, J % 4>(F, R, S);
     });
 }
 
@@ -395,16 +426,18 @@ __device__ __forceinline__ void mfma_block(f16v_t (&acc)[NB][NA], const Frags<NA
         mfma_vgpr_acc(acc[x][i], F.b[x], F.a[i]);
 }
 
-// One 16-K step in program order: the NA * NB MFMAs, each followed by its share of the NL
-// loads and the NJ VALU jobs that prepare the next step, fenced so that the compiler keeps
-// this order (a VALU job issues while the MFMA before it runs; loads reach the memory
-// pipeline spread over the step).
-template <int NM, int NJ, int NL, class M, class J, class L>
-__device__ __forceinline__ void bundled_step(M&& mfma, J&& job, L&& load)
+// One 16-K step in program order: the NA * NB MFMAs, each followed by its share of the NR
+// LDS reads, the NL loads and the NJ VALU jobs that prepare later steps, fenced so that the
+// compiler keeps this order (a VALU job issues while the MFMA before it runs; reads and
+// loads reach the LDS and memory pipelines spread over the step instead of in a burst that
+// the four waves would queue on).
+template <int NM, int NJ, int NL, int NR, class M, class J, class L, class R>
+__device__ __forceinline__ void bundled_step(M&& mfma, J&& job, L&& load, R&& read)
 {
     static_for<0, NM>([&](auto q) {
         constexpr int Q = decltype(q)::value;
         mfma(q);
+        static_for<Q * NR / NM, (Q + 1) * NR / NM>(read);
         static_for<Q * NL / NM, (Q + 1) * NL / NM>(load);
         static_for<Q * NJ / NM, (Q + 1) * NJ / NM>(job);
         __builtin_amdgcn_sched_barrier(0);
@@ -547,70 +580,88 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     static_for<0, S>([&](auto t) { issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave); });
     wait_vm<(S - 1) * Gm::OPS>();   // superstep 0 has landed (this wave's part)
     barrier_lds();
-    RawHalf<NA, NB> h0[2], h1;
+    constexpr bool FULL = Gm::FULL_READS;
+    constexpr int W = FULL ? 4 : 2;
+    RawCodes<NA, NB, W> rc[2];   // a superstep's codes (FULL) or its first half
+    RawCodes<NA, NB, 2> h1;      // the second half (not FULL)
     RawScales<NA, NB> rs[2];
     Scales<NA, NB> sc[2];
     Frags<NA, NB> fr[2];
-    read_half<NA, NB, 0>(h0[0], smem, code_off);
+    read_codes<NA, NB, W, 0>(rc[0], smem, code_off);
     read_scales<NA, NB>(rs[0], smem, scale_off);
     convert_scales<NA, NB>(sc[0], rs[0]);
-    convert_step<NA, NB, 0>(fr[0], h0[0], sc[0]);
+    convert_step<NA, NB, 0, 0>(fr[0], rc[0], sc[0]);
 
-    // One superstep t (its first half in h0[P], scales in sc[P], step 0's fragments in
-    // fr[0]).  Its second half is read at once; steps 0 and 1 run (MFMAs of a step beside
-    // the next step's conversions).  Then the wave waits for its own loads of superstep
-    // t+1, and the barrier publishes them and frees slot cs (superstep t: both halves have
-    // been read by every wave), which is refilled with superstep t+S; the first half and
-    // the scales of superstep t+1 are read, and steps 2 and 3 run, step 3 beside the
-    // conversion of step 0 of superstep t+1.  In the last superstep the "next" reads and
+    // One superstep t (its codes, or their first half, in rc[P], scales in sc[P], step 0's
+    // fragments in fr[0]).  Unless its whole codes are already in rc[P], the second half is
+    // read at once; steps 0 and 1 run (MFMAs of a step beside the next step's
+    // conversions).  Then the wave waits for its own loads of superstep t+1, and the
+    // barrier publishes them and frees slot cs (superstep t has been read by every wave),
+    // which is refilled with superstep t+S; the codes (or first half) and the scales of
+    // superstep t+1 are read, and steps 2 and 3 run, step 3 beside the conversion of step 0
+    // of superstep t+1.  In the last superstep the "next" reads and
     // conversions touch no superstep's bytes: harmless, and their results are unused.
     // Every superstep refills its slot (with zeros beyond the last superstep) and waits with
     // the same count; the refill's loads are spread over step 2.
     constexpr int NM = NA * NB;
     constexpr int NJ = 4 * Gm::NBLK;   // VALU jobs of one step's conversion
-    const auto no_load = [](auto) {};
+    const auto no_op = [](auto) {};
     int cs = 0;
     const auto superstep = [&](auto P_, int t) {
         constexpr int P = decltype(P_)::value;
         const int ns = cs + 1 == S ? 0 : cs + 1;
-        read_half<NA, NB, 1>(h1, smem + cs * Gm::SLOT, code_off);
-        __builtin_amdgcn_sched_barrier(0);   // the LDS reads go out first
-        bundled_step<NM, NJ, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[0]); },
+        const uint8_t* cur = smem + cs * Gm::SLOT;
+        const uint8_t* nxt = smem + ns * Gm::SLOT;
+        // step 0 (and, with half reads, the second half's reads)
+        bundled_step<NM, NJ, 0, FULL ? 0 : Gm::NBLK>(
+            [&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[0]); },
+            [&](auto j) {
+                constexpr int J = decltype(j)::value;
+                convert_dword<NA, NB, 1, 1, J / 4, J % 4>(fr[1], rc[P], sc[P]);
+            },
+            no_op, [&](auto y) { read_code<NA, NB, 2, 8, decltype(y)::value>(h1, cur, code_off); });
+        bundled_step<NM, NJ, 0, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[1]); },
                                 [&](auto j) {
                                     constexpr int J = decltype(j)::value;
-                                    convert_dword<NA, NB, 1, J / 4, J % 4>(fr[1], h0[P], sc[P]);
+                                    if constexpr (FULL)
+                                        convert_dword<NA, NB, 2, 2, J / 4, J % 4>(fr[0], rc[P], sc[P]);
+                                    else
+                                        convert_dword<NA, NB, 2, 0, J / 4, J % 4>(fr[0], h1, sc[P]);
                                 },
-                                no_load);
-        bundled_step<NM, NJ, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[1]); },
-                                [&](auto j) {
-                                    constexpr int J = decltype(j)::value;
-                                    convert_dword<NA, NB, 2, J / 4, J % 4>(fr[0], h1, sc[P]);
-                                },
-                                no_load);
+                                no_op, no_op);
         wait_vm<(S - 2) * Gm::OPS>();
         barrier_lds();
-        read_half<NA, NB, 0>(h0[1 - P], smem + ns * Gm::SLOT, code_off);
-        read_scales<NA, NB>(rs[1 - P], smem + ns * Gm::SLOT, scale_off);
-        __builtin_amdgcn_sched_barrier(0);
         const auto step2_jobs = [&](auto j) {
             constexpr int J = decltype(j)::value;
-            convert_dword<NA, NB, 3, J / 4, J % 4>(fr[1], h1, sc[P]);
+            if constexpr (FULL)
+                convert_dword<NA, NB, 3, 3, J / 4, J % 4>(fr[1], rc[P], sc[P]);
+            else
+                convert_dword<NA, NB, 3, 1, J / 4, J % 4>(fr[1], h1, sc[P]);
         };
         const auto step2_mfma = [&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[0]); };
-        const Refill<NA, NB> R = refill_of<NA, NB>(L, smem + cs * Gm::SLOT, t + S, kt_of(t + S));
-        bundled_step<NM, NJ, Gm::OPS>(step2_mfma, step2_jobs,
-                                      [&](auto op) { issue_op<NA, NB, decltype(op)::value>(L, R, wave); });
+        const Refill<NA, NB> R = refill_of<NA, NB>(L, const_cast<uint8_t*>(cur), t + S, kt_of(t + S));
+        // step 2, with the refill's loads and the reads of superstep t+1 (scales first, which
+        // step 3 converts first)
+        bundled_step<NM, NJ, Gm::OPS, 2 * Gm::NBLK>(
+            step2_mfma, step2_jobs, [&](auto op) { issue_op<NA, NB, decltype(op)::value>(L, R, wave); },
+            [&](auto r) {
+                constexpr int RD = decltype(r)::value;
+                if constexpr (RD < Gm::NBLK)
+                    read_scale<NA, NB, RD>(rs[1 - P], nxt, scale_off);
+                else
+                    read_code<NA, NB, W, 0, RD - Gm::NBLK>(rc[1 - P], nxt, code_off);
+            });
         // step 3: first the next superstep's scales, then its step 0 fragments
-        bundled_step<NM, NJ + Gm::NBLK, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[1]); },
+        bundled_step<NM, NJ + Gm::NBLK, 0, 0>([&](auto q) { mfma_block<NA, NB, decltype(q)::value>(acc, fr[1]); },
                                            [&](auto j) {
                                                constexpr int J = decltype(j)::value;
                                                if constexpr (J < Gm::NBLK)
                                                    convert_scale<NA, NB, J>(sc[1 - P], rs[1 - P]);
                                                else
-                                                   convert_dword<NA, NB, 0, (J - Gm::NBLK) / 4, (J - Gm::NBLK) % 4>(
-                                                       fr[0], h0[1 - P], sc[1 - P]);
+                                                   convert_dword<NA, NB, 0, 0, (J - Gm::NBLK) / 4, (J - Gm::NBLK) % 4>(
+                                                       fr[0], rc[1 - P], sc[1 - P]);
                                            },
-                                           no_load);
+                                           no_op, no_op);
         cs = ns;
     };
     for (int t = 0; t < nsup; t += 2) {
