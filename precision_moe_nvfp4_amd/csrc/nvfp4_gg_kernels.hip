@@ -115,7 +115,12 @@ struct Geo {
     static constexpr bool FULL_READS = NACC < 20 && NBLK < 11;
     // epilogue exchange: per block, 4 element groups x 3 partner copies x 1 KiB
     static constexpr int RED_BLK = 3 * 4 * 1024;
-    static constexpr int RED_ROUND = (LDS_BYTES / RED_BLK) < NACC ? (LDS_BYTES / RED_BLK) : NACC;
+    // the exchange region starts after ring slots 0 .. SLOTS-2, which may meanwhile take the
+    // first supersteps of the workgroup's next unit
+    static constexpr int RED_AT = (SLOTS - 1) * SLOT;
+    static constexpr int RED_FIT = (LDS_BYTES - RED_AT) / RED_BLK;
+    static constexpr int RED_ROUND = RED_FIT < NACC ? RED_FIT : NACC;
+    static_assert(RED_FIT >= 1, "the exchange region must hold one block");
     static_assert(SLOTS >= 3, "a unit shape needs at least 3 ring slots");
     static_assert((SLOTS - 2) * OPS <= 63, "the steady-state wait count must fit vmcnt");
 };
@@ -482,8 +487,12 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
     constexpr int RR = Gm::RED_ROUND;
     const int j = lane & 31, h = lane >> 5;
     const bool vec = (ldc & 3) == 0;
+    // every row and column of the unit exists and rows are 8-byte aligned: no store masks
+    const bool interior = rows == 32 * NA && cols == 32 * NB && vec;
     // exchange place of element group q's copy from partner slot sl, round block xr
-    const auto at = [&](int xr, int q, int sl) { return smem + (((xr * 4 + q) * 3 + sl) * 64 + lane) * 16; };
+    const auto at = [&](int xr, int q, int sl) {
+        return smem + Gm::RED_AT + (((xr * 4 + q) * 3 + sl) * 64 + lane) * 16;
+    };
     static_for<0, (Gm::NACC + RR - 1) / RR>([&](auto rd) {
         constexpr int R0 = decltype(rd)::value * RR;
         constexpr int NR = Gm::NACC - R0 < RR ? Gm::NACC - R0 : RR;
@@ -522,7 +531,11 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
             });
             const int r = 32 * ib + j;
             const int cc = 32 * xb + 8 * W + 4 * h;
-            if (r < rows) {
+            if (interior) {
+                *reinterpret_cast<u2_t*>(c0 + (long)r * ldc + cc) =
+                    u2_t{(uint32_t)f16_bits_rne(v[0]) | ((uint32_t)f16_bits_rne(v[1]) << 16),
+                         (uint32_t)f16_bits_rne(v[2]) | ((uint32_t)f16_bits_rne(v[3]) << 16)};
+            } else if (r < rows) {
                 uint16_t* crow = c0 + (long)r * ldc;
                 const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
                 const uint16_t h2 = f16_bits_rne(v[2]), h3 = f16_bits_rne(v[3]);
@@ -546,13 +559,23 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
 // One unit
 // ---------------------------------------------------------------------------------------
 
-// Rows [row0, row0 + rows) of group G times columns [col0, col0 + cols), the whole K of the
-// group.  All four waves run the same sequence of loads and barriers.
+// One unit of the schedule: group gi, rows [row0, row0 + rows) times columns
+// [col0, col0 + cols), unit shape na x nb.
+struct Unit {
+    int gi, row0, rows, col0, cols, na, nb;
+};
+
+// Unit cu over the whole K of its group.  If `prefetched`, the previous unit already issued
+// this unit's supersteps 0 .. S-2 (same shape); if `pf_next`, this unit issues those of the
+// next unit nx (same shape) before its own epilogue, so that their fetch overlaps the
+// K reduction and the C stores.  All four waves run the same sequence of loads and barriers.
 template <int NA, int NB>
-__device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, int rows, int col0, int cols,
-                                                   int ldc, bool blocked, uint8_t* smem)
+__device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, bool prefetched, bool pf_next,
+                                         const Unit& nx, bool blocked, uint8_t* smem)
 {
     using Gm = gk::Geo<NA, NB>;
+    const GroupArgs& G = A.grp[cu.gi];
+    const int k = G.k, row0 = cu.row0, rows = cu.rows, col0 = cu.col0, cols = cu.cols, ldc = G.ldc;
     constexpr int S = Gm::SLOTS;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -563,8 +586,16 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     // superstep issues the same loads and waits with the same count)
     const auto kt_of = [&](int t) { return t < nsup - 1 ? gk::SK : t == nsup - 1 ? klast : 0; };
 
-    wait_vm<0>();   // the previous unit's stores are out of the count
+    // The ring's first S supersteps go out first (only the last of them if the previous unit
+    // issued the others).  The previous unit's C stores may still be in flight: they touch
+    // neither LDS nor this unit's operands, and loads complete in issue order among
+    // themselves, so whatever the stores do, the wait below means that superstep 0 has
+    // landed.
     const UnitLoads<NA, NB> L = unit_loads<NA, NB>(G, k, row0, rows, col0, cols, blocked, wave, lane);
+    if (!prefetched)
+        static_for<0, S - 1>([&](auto t) { issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave); });
+    issue_superstep<NA, NB>(L, smem + (S - 1) * Gm::SLOT, S - 1, kt_of(S - 1), wave);
+    __builtin_amdgcn_sched_barrier(0);
 
     f16v_t acc[NB][NA];
 #pragma unroll
@@ -577,7 +608,6 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     const int code_off = j * gk::ROWB + 16 * ((2 * wave + h) ^ gk::swz(j));
     const int scale_off = (j >> 3) * Gm::SREG + 16 * (j & 7) + 4 * wave + 2 * h;
 
-    static_for<0, S>([&](auto t) { issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave); });
     wait_vm<(S - 1) * Gm::OPS>();   // superstep 0 has landed (this wave's part)
     barrier_lds();
     constexpr bool FULL = Gm::FULL_READS;
@@ -670,6 +700,20 @@ __device__ __forceinline__ void run_unit(const GroupArgs& G, int k, int row0, in
     }
     wait_vm<0>();   // the zero refills beyond the last superstep have landed before the LDS is reused
 
+    if (pf_next) {
+        // every wave has read the ring for the last time: slots 0 .. S-2 take the next unit's
+        // first supersteps (the exchange region lies beyond them)
+        barrier_lds();
+        const GroupArgs& Gn = A.grp[nx.gi];
+        const int nsup_n = (Gn.k + gk::SK - 1) / gk::SK;
+        const int klast_n = Gn.k - gk::SK * (nsup_n - 1);
+        const UnitLoads<NA, NB> Ln =
+            unit_loads<NA, NB>(Gn, Gn.k, nx.row0, nx.rows, nx.col0, nx.cols, blocked, wave, lane);
+        static_for<0, S - 1>([&](auto t) {
+            const int kt = t < nsup_n - 1 ? gk::SK : t == nsup_n - 1 ? klast_n : 0;
+            issue_superstep<NA, NB>(Ln, smem + t * Gm::SLOT, t, kt, wave);
+        });
+    }
     drain_vgpr_acc<NA, NB>(acc);
     uint16_t* c0 = G.c + (long)row0 * ldc + col0;
     switch (wave) {
@@ -711,8 +755,10 @@ __global__ __launch_bounds__(gk::THREADS) void nvfp4_gg_units(KernArgs args_byva
     const long U = A.units;
     const int u0 = (int)(U * v / V), u1 = (int)(U * (v + 1) / V);
     const bool blocked = (A.flags & kFlagBlockedScales) != 0;
+    if (u0 >= u1) return;
     int gi = 0, gbase = 0;
-    for (int u = u0; u < u1; ++u) {
+    // unit u's group and tile (units in increasing order: the group walk only moves on)
+    const auto decode = [&](int u) {
         int cnt = group_units(A.grp[gi]);
         while (u >= gbase + cnt && gi + 1 < A.g) {
             gbase += cnt;
@@ -726,16 +772,26 @@ __global__ __launch_bounds__(gk::THREADS) void nvfp4_gg_units(KernArgs args_byva
         const int l = u - gbase;
         const int rc = l % rch, ct = l / rch;
         const int row0 = rc * 32 * na, col0 = ct * 32 * nb;
-        const int rows = min(32 * na, m - row0), cols = min(32 * nb, G.n - col0);
-        switch ((na << 8) | nb) {
+        return Unit{gi, row0, min(32 * na, m - row0), col0, min(32 * nb, G.n - col0), na, nb};
+    };
+    Unit cu = decode(u0);
+    bool prefetched = false;
+    for (int u = u0; u < u1; ++u) {
+        const bool has_next = u + 1 < u1;
+        const Unit nx = has_next ? decode(u + 1) : cu;
+        const bool pf_next = has_next && nx.na == cu.na && nx.nb == cu.nb;
+        switch ((cu.na << 8) | cu.nb) {
 #define NVFP4GG_CASE(NA_, NB_) \
-    case ((NA_) << 8) | (NB_): run_unit<NA_, NB_>(G, G.k, row0, rows, col0, cols, G.ldc, blocked, smem); break;
+    case ((NA_) << 8) | (NB_): run_unit<NA_, NB_>(A, cu, prefetched, pf_next, nx, blocked, smem); break;
             NVFP4GG_UNIT_SHAPES(NVFP4GG_CASE)
 #undef NVFP4GG_CASE
         default: break;
         }
+        prefetched = pf_next;
+        cu = nx;
     }
 }
+
 
 hipError_t launch_units(const KernArgs& args, int grid, hipStream_t stream)
 {
