@@ -71,7 +71,7 @@ def test_blocked_gemm_matches_oracle_and_row_major(m, n, k):
     say(f"blocked gemm m={m} n={n} k={k}")
     inp = make_inputs(m, n, k, seed=sum(m) + n + k)
     got = run_gpu_blocked(inp)
-    check(inp, got, f"blocked {m} {n} {k}")
+    check(inp, got, f"blocked {m} {n} {k}", exact=True)
     ref = run_gpu(inp)
     for i in range(inp.g):
         assert np.array_equal(got[i], ref[i]), f"group {i}: blocked and row-major runs differ"
@@ -82,4 +82,4 @@ def test_blocked_gemm_full_size(name):
     cfg = CONFIGS[name]
     say(f"blocked gemm {name}: {cfg}")
     inp = make_inputs(cfg.m, cfg.n, cfg.k, cfg.seed)
-    check(inp, run_gpu_blocked(inp), f"blocked {name}")
+    check(inp, run_gpu_blocked(inp), f"blocked {name}", exact=True)

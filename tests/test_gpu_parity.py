@@ -3,8 +3,10 @@
 Bar (per element): |gpu - ref| <= 2 ulp16(ref) + 1e-5 * sum_k |a*sa*b*sb|, with ref the
 oracle's fp16 value; infinities must match exactly.  Every C_i is surrounded by canary
 halves (a NaN pattern) to prove that each element is written exactly inside its bounds.
-The fp16 bit-mismatch count (expected 0: the fp32 sums of these inputs are exact) is
-printed as a diagnostic.
+On the inputs of the workload recipe (scale codes 8..32) the GPU's fp16 must also equal the
+oracle's bit for bit (exact=True): products are multiples of 2^-20 and the fp32 partial sums of
+these seeded inputs stay where fp32 still holds them exactly (it does not once a partial sum
+reaches 2^4, which the extreme-scale cases below do, so there only the bar applies).
 """
 import numpy as np
 import pytest
@@ -44,7 +46,7 @@ def run_gpu(inp, stream=None, plan=None):
     return out
 
 
-def check(inp, got, label):
+def check(inp, got, label, exact=False):
     ref = oracle.grouped_inputs(inp, want_abs=True)
     total_bad = total_mis = total = 0
     for i in range(inp.g):
@@ -65,13 +67,15 @@ def check(inp, got, label):
             say(f"{label}: group {i} first bad ({r},{c}) gpu={gv[r, c]} ref={rv[r, c]} tol={tol[r, c]}")
     say(f"{label}: {total} elements, {total_bad} beyond tolerance, {total_mis} fp16 bit mismatches")
     assert total_bad == 0
+    if exact:
+        assert total_mis == 0, f"{label}: {total_mis} fp16 bit mismatches"
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
 def test_configs_full_size(name):
     say(f"parity {name}: {CONFIGS[name]}")
     inp = make_inputs(CONFIGS[name].m, CONFIGS[name].n, CONFIGS[name].k, CONFIGS[name].seed)
-    check(inp, run_gpu(inp), name)
+    check(inp, run_gpu(inp), name, exact=True)
 
 
 @pytest.mark.parametrize("m,n,k", [
@@ -81,7 +85,7 @@ def test_configs_full_size(name):
 def test_ragged_and_edge_shapes(m, n, k):
     say(f"parity ragged m={m} n={n} k={k}")
     inp = make_inputs(m, n, k, seed=len(m) * 1000 + n + k)
-    check(inp, run_gpu(inp), f"ragged m={m} n={n} k={k}")
+    check(inp, run_gpu(inp), f"ragged m={m} n={n} k={k}", exact=True)
 
 
 def test_every_e4m3fn_code_and_negative_scales():
@@ -114,7 +118,7 @@ def test_repeatable_and_stream_aware():
         second = run_gpu(inp, stream=s, plan=plan)
     for a, b in zip(first, second):
         assert np.array_equal(a, b)
-    check(inp, first, "repeatable")
+    check(inp, first, "repeatable", exact=True)
 
 
 def test_misaligned_pointer_is_rejected_on_device():

@@ -64,7 +64,7 @@ def check_outputs(problems, bufs, inps, what):
         c = h[PAD:PAD + m * ld].reshape(m, ld)
         assert np.all(c[:, n:] == CANARY), f"group {i}: write beyond column n"
         if m:
-            check(inp, [np.ascontiguousarray(c[:, :n])], f"{what}: group {i} (m={m} n={n} k={k} ldc={ldc})")
+            check(inp, [np.ascontiguousarray(c[:, :n])], f"{what}: group {i} (m={m} n={n} k={k} ldc={ldc})", exact=True)
 
 
 @pytest.mark.parametrize("layout", [gg.SCALES_ROW_MAJOR, gg.SCALES_BLOCKED])

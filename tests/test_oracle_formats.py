@@ -79,3 +79,15 @@ def test_ulp16_definition_points():
     bits = np.array([0x0000, 0x0001, 0x0400, 0x3C00, 0x7BFF, 0xBC00], dtype=np.uint16)
     u = oracle.ulp16(bits)
     assert list(u) == [2.0 ** -24, 2.0 ** -24, 2.0 ** -24, 2.0 ** -10, 32.0, 2.0 ** -10]
+
+
+def test_tolerance_is_two_ulp16_plus_abssum_term():
+    # hand-computed bounds: fp16 1.0 (0x3C00) has spacing 2^-10, 2048.0 (0x6800) has 2,
+    # 0 and subnormals 2^-24, -0.5 (0xB800) 2^-11, an infinity the top binade's 32
+    bits = np.array([0x3C00, 0x6800, 0x0000, 0x0001, 0xB800, 0x7C00], np.uint16)
+    abssum = np.array([0.0, 100.0, 1.0, 0.0, 3.0, 0.0])
+    want = np.array([2 * 2.0 ** -10, 2 * 2.0 + 1e-3, 2 * 2.0 ** -24 + 1e-5, 2 * 2.0 ** -24,
+                     2 * 2.0 ** -11 + 3e-5, 2 * 32.0])
+    assert np.allclose(oracle.tolerance(bits, abssum), want, rtol=0, atol=1e-15)
+    # the bound scales with the abssum term alone when the value is 0
+    assert oracle.tolerance(np.array([0], np.uint16), np.array([1e6]))[0] == 2 * 2.0 ** -24 + 10.0
