@@ -226,3 +226,15 @@ def test_build_script_loads_without_the_package():
             "assert 'precision_moe_nvfp4_amd' not in sys.modules, 'package imported'")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     subprocess.run([sys.executable, "-c", code], cwd=root, check=True)
+
+
+def test_library_imports_no_allocation_copy_or_device_sync():
+    # the plan is host memory and a call is one launch: the library does not even link the HIP
+    # entry points that allocate, copy, free or synchronise the device
+    out = subprocess.run(["nm", "-D", "--undefined-only", gg.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    for forbidden in ("hipMalloc", "hipFree", "hipMemcpy", "hipMemcpyAsync", "hipMemset", "hipMemsetAsync",
+                      "hipDeviceSynchronize", "hipStreamSynchronize", "hipHostMalloc", "hipExtMallocWithFlags"):
+        assert forbidden not in imported, forbidden
+    assert "hipLaunchKernel" in imported
