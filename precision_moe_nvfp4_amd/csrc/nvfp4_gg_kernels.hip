@@ -493,6 +493,10 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
     const auto at = [&](int xr, int q, int sl) {
         return smem + Gm::RED_AT + (((xr * 4 + q) * 3 + sl) * 64 + lane) * 16;
     };
+    // this lane's first C element of row block ib (row 32 ib + j, columns 8 W + 4 h ..)
+    uint16_t* rowp[NA];
+#pragma unroll
+    for (int ib = 0; ib < NA; ++ib) rowp[ib] = c0 + (long)(32 * ib + j) * ldc + 8 * W + 4 * h;
     static_for<0, (Gm::NACC + RR - 1) / RR>([&](auto rd) {
         constexpr int R0 = decltype(rd)::value * RR;
         constexpr int NR = Gm::NACC - R0 < RR ? Gm::NACC - R0 : RR;
@@ -512,27 +516,34 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
             __builtin_amdgcn_sched_barrier(0);   // one block's copies at a time (register pressure)
         });
         barrier_lds();
-        // read the partner copies one block ahead of the sums that use them
-        u4_t o[2][3];
-        static_for<0, 3>([&](auto sl) { o[0][decltype(sl)::value] = *reinterpret_cast<const u4_t*>(at(0, W, sl)); });
+        // read the partner copies RD blocks ahead of the sums that use them
+        constexpr int RD = 4;
+        u4_t o[RD][3];
+        static_for<0, (RD - 1 < NR ? RD - 1 : NR)>([&](auto x_) {
+            constexpr int X = decltype(x_)::value;
+            static_for<0, 3>([&](auto sl) {
+                o[X % RD][decltype(sl)::value] = *reinterpret_cast<const u4_t*>(at(X, W, sl));
+            });
+        });
         static_for<0, NR>([&](auto xr_) {
             constexpr int XR = decltype(xr_)::value;
             constexpr int xb = (R0 + XR) / NA, ib = (R0 + XR) % NA;
-            if constexpr (XR + 1 < NR)
+            if constexpr (XR + RD - 1 < NR)
                 static_for<0, 3>([&](auto sl) {
-                    o[(XR + 1) & 1][decltype(sl)::value] = *reinterpret_cast<const u4_t*>(at(XR + 1, W, sl));
+                    o[(XR + RD - 1) % RD][decltype(sl)::value] =
+                        *reinterpret_cast<const u4_t*>(at(XR + RD - 1, W, sl));
                 });
             __builtin_amdgcn_sched_barrier(0);
             float v[4];
             static_for<0, 4>([&](auto e_) {
                 constexpr int E = decltype(e_)::value;
-                v[E] = acc[xb][ib][4 * W + E] + __uint_as_float(o[XR & 1][0][E]) + __uint_as_float(o[XR & 1][1][E]) +
-                       __uint_as_float(o[XR & 1][2][E]);
+                v[E] = acc[xb][ib][4 * W + E] + __uint_as_float(o[XR % RD][0][E]) +
+                       __uint_as_float(o[XR % RD][1][E]) + __uint_as_float(o[XR % RD][2][E]);
             });
             const int r = 32 * ib + j;
             const int cc = 32 * xb + 8 * W + 4 * h;
             if (interior) {
-                *reinterpret_cast<u2_t*>(c0 + (long)r * ldc + cc) =
+                *reinterpret_cast<u2_t*>(rowp[ib] + 32 * xb) =
                     u2_t{(uint32_t)f16_bits_rne(v[0]) | ((uint32_t)f16_bits_rne(v[1]) << 16),
                          (uint32_t)f16_bits_rne(v[2]) | ((uint32_t)f16_bits_rne(v[3]) << 16)};
             } else if (r < rows) {
@@ -577,8 +588,13 @@ __device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, bool
     const GroupArgs& G = A.grp[cu.gi];
     const int k = G.k, row0 = cu.row0, rows = cu.rows, col0 = cu.col0, cols = cu.cols, ldc = G.ldc;
     constexpr int S = Gm::SLOTS;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the thread index through an instruction the compiler cannot hoist: values derived from
+    // it are then recomputed per unit instead of being kept live across all of them (the
+    // kernel has no scratch)
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nsup = (k + gk::SK - 1) / gk::SK;
     const int klast = k - gk::SK * (nsup - 1);
     // K values of superstep t: 256, the tail in the last, none beyond (such supersteps are
@@ -597,11 +613,18 @@ __device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, bool
     issue_superstep<NA, NB>(L, smem + (S - 1) * Gm::SLOT, S - 1, kt_of(S - 1), wave);
     __builtin_amdgcn_sched_barrier(0);
 
+    // The accumulators start at zero.  The zero comes from an instruction the compiler cannot
+    // hoist: a zero vector hoisted out of the unit loop would stay live across every unit and
+    // be spilled to scratch (and a kernel with a larger scratch allocation launches its waves
+    // markedly slower: measured 2x on the 1-unit-per-workgroup shapes at 96 bytes per lane).
+    float zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const f16v_t zv = {zero, zero, zero, zero, zero, zero, zero, zero, zero, zero, zero, zero, zero, zero, zero, zero};
     f16v_t acc[NB][NA];
 #pragma unroll
     for (int x = 0; x < NB; ++x)
 #pragma unroll
-        for (int i = 0; i < NA; ++i) acc[x][i] = f16v_t{};
+        for (int i = 0; i < NA; ++i) acc[x][i] = zv;
 
     // this lane's LDS read offsets inside a slot (wave's K quarter, lane half h, row j)
     const int j = lane & 31, h = lane >> 5;

@@ -238,3 +238,48 @@ def test_library_imports_no_allocation_copy_or_device_sync():
                       "hipDeviceSynchronize", "hipStreamSynchronize", "hipHostMalloc", "hipExtMallocWithFlags"):
         assert forbidden not in imported, forbidden
     assert "hipLaunchKernel" in imported
+
+
+def _kernel_metadata():
+    """The unit kernel's code-object metadata (registers, LDS, scratch) read from the built
+    library's gfx950 code object with the ROCm LLVM tools; None when they are missing."""
+    import os
+    import shutil
+    import tempfile
+    llvm = "/opt/rocm/llvm/bin"
+    tools = [os.path.join(llvm, t) for t in ("clang-offload-bundler", "llvm-readelf")]
+    if not all(os.path.exists(t) for t in tools) or shutil.which("objcopy") is None:
+        return None
+    with tempfile.TemporaryDirectory() as d:
+        fat, co = os.path.join(d, "fat.bin"), os.path.join(d, "k.co")
+        subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", gg.LIB_PATH], check=True,
+                       capture_output=True)
+        subprocess.run([tools[0], "--unbundle", "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                        f"--input={fat}", f"--output={co}"], check=True, capture_output=True)
+        notes = subprocess.run([tools[1], "--notes", co], check=True, capture_output=True, text=True).stdout
+    meta, cur = {}, None
+    for line in notes.splitlines():
+        line = line.strip().lstrip("- ")
+        if ":" not in line:
+            continue
+        key, val = (s.strip() for s in line.split(":", 1))
+        if key == ".agpr_count":
+            cur = {key: val}
+        elif cur is not None:
+            cur[key] = val
+            if key == ".name":
+                meta[val] = cur
+    return meta
+
+
+def test_unit_kernel_uses_no_scratch():
+    # the unit kernel keeps everything in registers and LDS: no scratch (a kernel with a larger
+    # scratch allocation launches its waves markedly slower), one workgroup's 160 KiB of LDS
+    meta = _kernel_metadata()
+    if meta is None:
+        pytest.skip("ROCm LLVM tools not available")
+    k = [v for name, v in meta.items() if "nvfp4_gg_units" in name]
+    assert len(k) == 1
+    assert int(k[0][".private_segment_fixed_size"]) == 0
+    assert int(k[0][".group_segment_fixed_size"]) == 160 * 1024
+    assert int(k[0][".vgpr_count"]) <= 512
