@@ -487,8 +487,9 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
     constexpr int RR = Gm::RED_ROUND;
     const int j = lane & 31, h = lane >> 5;
     const bool vec = (ldc & 3) == 0;
-    // every row and column of the unit exists and rows are 8-byte aligned: no store masks
-    const bool interior = rows == 32 * NA && cols == 32 * NB && vec;
+    // every column of the unit exists and rows are 8-byte aligned: one 8-byte store per lane,
+    // masked by the row only (and not at all when every row exists)
+    const bool colfull = cols == 32 * NB && vec;
     // exchange place of element group q's copy from partner slot sl, round block xr
     const auto at = [&](int xr, int q, int sl) {
         return smem + Gm::RED_AT + (((xr * 4 + q) * 3 + sl) * 64 + lane) * 16;
@@ -542,10 +543,11 @@ __device__ __forceinline__ void epilogue_w(const f16v_t (&acc)[NB][NA], uint8_t*
             });
             const int r = 32 * ib + j;
             const int cc = 32 * xb + 8 * W + 4 * h;
-            if (interior) {
-                *reinterpret_cast<u2_t*>(rowp[ib] + 32 * xb) =
-                    u2_t{(uint32_t)f16_bits_rne(v[0]) | ((uint32_t)f16_bits_rne(v[1]) << 16),
-                         (uint32_t)f16_bits_rne(v[2]) | ((uint32_t)f16_bits_rne(v[3]) << 16)};
+            if (colfull) {
+                if (r < rows)
+                    *reinterpret_cast<u2_t*>(rowp[ib] + 32 * xb) =
+                        u2_t{(uint32_t)f16_bits_rne(v[0]) | ((uint32_t)f16_bits_rne(v[1]) << 16),
+                             (uint32_t)f16_bits_rne(v[2]) | ((uint32_t)f16_bits_rne(v[3]) << 16)};
             } else if (r < rows) {
                 uint16_t* crow = c0 + (long)r * ldc;
                 const uint16_t h0 = f16_bits_rne(v[0]), h1 = f16_bits_rne(v[1]);
