@@ -583,11 +583,10 @@ struct Unit {
 // next unit nx (same shape) before its own epilogue, so that their fetch overlaps the
 // K reduction and the C stores.  All four waves run the same sequence of loads and barriers.
 template <int NA, int NB>
-__device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, bool prefetched, bool pf_next,
+__device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, const GroupArgs G, bool prefetched, bool pf_next,
                                          const Unit& nx, bool blocked, uint8_t* smem)
 {
     using Gm = gk::Geo<NA, NB>;
-    const GroupArgs& G = A.grp[cu.gi];
     const int k = G.k, row0 = cu.row0, rows = cu.rows, col0 = cu.col0, cols = cu.cols, ldc = G.ldc;
     constexpr int S = Gm::SLOTS;
     // the thread index through an instruction the compiler cannot hoist: values derived from
@@ -753,53 +752,88 @@ __device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, bool
 // Persistent grouped scheduler
 // ---------------------------------------------------------------------------------------
 
-// Units of group G: ceil(m / 32 na) row chunks times ceil(n / 32 nb) column tiles.
-__device__ __forceinline__ int group_units(const GroupArgs& G)
-{
-    const int m = G.m_shape & kMMask;
-    if (m == 0) return 0;
-    const int na = (G.m_shape >> kNaShift) & 15, nb = (G.m_shape >> kNbShift) & 31;
-    return ((m + 32 * na - 1) / (32 * na)) * ((G.n + 32 * nb - 1) / (32 * nb));
-}
-
 // Workgroup b is virtual workgroup v = (b % 8) * vq + b / 8 of V = 8 vq (workgroups are
 // dealt to the 8 XCDs round-robin, so consecutive v share an XCD and its L2); it runs
 // the units [U v / V, U (v+1) / V) of the unit sequence, which lists every group's units
 // in schedule order, row chunks fastest (so the units that read one B column tile are
 // consecutive).  This is the prefix-sum tile enumeration of the persistent scheduler on
-// the page "kernelindex submission 503584" (group found by walking the per-group unit
-// counts, tile decoded from the rank inside the group).
+// the page "kernelindex submission 503584" (a group's units are ceil(m / 32 na) row chunks
+// times ceil(n / 32 nb) column tiles; a unit's group is found from the running sums of these
+// counts, its tile from its rank inside the group).
+constexpr int kEagerGroups = 8;
+
 __global__ __launch_bounds__(gk::THREADS) void nvfp4_gg_units(KernArgs args_byval)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[gk::LDS_BYTES];
     (void)args_byval;
     const KernArgs& A = *(const KernArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    // Lane l reads entry l of the group table, the first kEagerGroups lanes together with the
+    // header (lanes < NVFP4_GG_MAX_GROUPS, so every read lies inside the kernel arguments).
+    // Units are then found from registers, and the first unit's group entry comes from them
+    // too: one memory round trip before the first operand load for tables of up to
+    // kEagerGroups groups (two beyond), where walking the table entry by entry costs one
+    // round trip per group passed.  Reading only a few entries eagerly keeps the requests of
+    // all waves at kernel start to a few cache lines.
+    const int lane0 = threadIdx.x & 63;
+    GroupArgs ent{};
+    if (lane0 < kEagerGroups) ent = A.grp[lane0];
+    // (used here together with the header, so that all of these reads are in flight at once)
+    asm volatile("" ::"v"(ent.a), "v"(ent.b), "v"(ent.sfa), "v"(ent.sfb), "v"(ent.c), "v"(ent.m_shape), "v"(ent.n),
+                 "v"(ent.k), "v"(ent.ldc), "s"(A.g), "s"(A.units), "s"(A.vq), "s"(A.flags));
+    // tables of more groups: the rest of the entries, now that g is known
+    if (lane0 >= kEagerGroups && lane0 < A.g) ent = A.grp[lane0];
     const int b = blockIdx.x;
-    const int vq = A.vq;
-    const long V = 8L * vq, v = (long)(b & 7) * vq + (b >> 3);
-    const long U = A.units;
-    const int u0 = (int)(U * v / V), u1 = (int)(U * (v + 1) / V);
+    const unsigned V = 8u * (unsigned)A.vq, v = (unsigned)(b & 7) * (unsigned)A.vq + (unsigned)(b >> 3);
+    // U v / V without 64-bit division: U = per V + rem, so U v / V = per v + rem v / V
+    // (rem v < V^2 fits in 32 bits)
+    const unsigned U = (unsigned)A.units, per = U / V, rem = U % V;
+    const int u0 = (int)(per * v + rem * v / V), u1 = (int)(per * (v + 1) + rem * (v + 1) / V);
     const bool blocked = (A.flags & kFlagBlockedScales) != 0;
     if (u0 >= u1) return;
-    int gi = 0, gbase = 0;
-    // unit u's group and tile (units in increasing order: the group walk only moves on)
-    const auto decode = [&](int u) {
-        int cnt = group_units(A.grp[gi]);
-        while (u >= gbase + cnt && gi + 1 < A.g) {
-            gbase += cnt;
-            ++gi;
-            cnt = group_units(A.grp[gi]);
+    const int g = A.g;
+    // lane l < g: group l's shape word, columns and first unit past its units (the running
+    // sum of the unit counts); lanes beyond g take no part
+    const int ms_l = ent.m_shape, n_l = ent.n;
+    int end_l = 0;
+    {
+        const int m = ms_l & kMMask, na = (ms_l >> kNaShift) & 15, nb = (ms_l >> kNbShift) & 31;
+        const int cnt = lane0 < g && m > 0 ? ((m + 32 * na - 1) / (32 * na)) * ((n_l + 32 * nb - 1) / (32 * nb)) : 0;
+        int sum = 0;
+        for (int i = 0; i < g; ++i) {
+            sum += __builtin_amdgcn_readlane(cnt, i);
+            if (lane0 == i) end_l = sum;
         }
-        const GroupArgs& G = A.grp[gi];
-        const int m = G.m_shape & kMMask;
-        const int na = (G.m_shape >> kNaShift) & 15, nb = (G.m_shape >> kNbShift) & 31;
+    }
+    // unit u's group (the first whose units end beyond u; the ends never decrease) and tile
+    const auto decode = [&](int u) {
+        const int gi = __popcll(__ballot(lane0 < g && end_l <= u));
+        const int gbase = gi > 0 ? __builtin_amdgcn_readlane(end_l, gi - 1) : 0;
+        const int ms = __builtin_amdgcn_readlane(ms_l, gi), n = __builtin_amdgcn_readlane(n_l, gi);
+        const int m = ms & kMMask;
+        const int na = (ms >> kNaShift) & 15, nb = (ms >> kNbShift) & 31;
         const int rch = (m + 32 * na - 1) / (32 * na);
         const int l = u - gbase;
         const int rc = l % rch, ct = l / rch;
         const int row0 = rc * 32 * na, col0 = ct * 32 * nb;
-        return Unit{gi, row0, min(32 * na, m - row0), col0, min(32 * nb, G.n - col0), na, nb};
+        return Unit{gi, row0, min(32 * na, m - row0), col0, min(32 * nb, n - col0), na, nb};
+    };
+    const auto lane_ptr = [](const void* p, int i) {
+        const unsigned long long x = (unsigned long long)p;
+        return (unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(unsigned)x, i) |
+               (unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(unsigned)(x >> 32), i) << 32;
     };
     Unit cu = decode(u0);
+    // the first unit's group entry, from the lane that read it
+    GroupArgs gcur;
+    gcur.a = (const uint8_t*)lane_ptr(ent.a, cu.gi);
+    gcur.b = (const uint8_t*)lane_ptr(ent.b, cu.gi);
+    gcur.sfa = (const uint8_t*)lane_ptr(ent.sfa, cu.gi);
+    gcur.sfb = (const uint8_t*)lane_ptr(ent.sfb, cu.gi);
+    gcur.c = (uint16_t*)lane_ptr(ent.c, cu.gi);
+    gcur.m_shape = __builtin_amdgcn_readlane(ent.m_shape, cu.gi);
+    gcur.n = __builtin_amdgcn_readlane(ent.n, cu.gi);
+    gcur.k = __builtin_amdgcn_readlane(ent.k, cu.gi);
+    gcur.ldc = __builtin_amdgcn_readlane(ent.ldc, cu.gi);
     bool prefetched = false;
     for (int u = u0; u < u1; ++u) {
         const bool has_next = u + 1 < u1;
@@ -807,15 +841,17 @@ __global__ __launch_bounds__(gk::THREADS) void nvfp4_gg_units(KernArgs args_byva
         const bool pf_next = has_next && nx.na == cu.na && nx.nb == cu.nb;
         switch ((cu.na << 8) | cu.nb) {
 #define NVFP4GG_CASE(NA_, NB_) \
-    case ((NA_) << 8) | (NB_): run_unit<NA_, NB_>(A, cu, prefetched, pf_next, nx, blocked, smem); break;
+    case ((NA_) << 8) | (NB_): run_unit<NA_, NB_>(A, cu, gcur, prefetched, pf_next, nx, blocked, smem); break;
             NVFP4GG_UNIT_SHAPES(NVFP4GG_CASE)
 #undef NVFP4GG_CASE
         default: break;
         }
         prefetched = pf_next;
         cu = nx;
+        if (has_next) gcur = A.grp[cu.gi];
     }
 }
+
 
 
 hipError_t launch_units(const KernArgs& args, int grid, hipStream_t stream)

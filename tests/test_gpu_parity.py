@@ -81,6 +81,10 @@ def test_configs_full_size(name):
 @pytest.mark.parametrize("m,n,k", [
     ([1], 16, 256), ([17, 1, 129], 200, 256), ([255, 0, 3], 130, 512), ([0, 0, 7], 64, 256),
     ([300], 1, 768), ([33, 65, 97, 129, 161], 384, 1024), ([2] * 64, 48, 256), ([384, 500], 136, 256),
+    # more groups than the kernel reads eagerly, empty ones among them (and at both ends)
+    ([0, 40, 0, 0, 130, 1, 0, 64, 0, 200, 0, 3, 0], 320, 512),
+    # the largest table, several units per group and several groups per workgroup
+    ([8 + (37 * i) % 153 for i in range(64)], 288, 512),
 ])
 def test_ragged_and_edge_shapes(m, n, k):
     say(f"parity ragged m={m} n={n} k={k}")
