@@ -83,6 +83,14 @@ constexpr int ROWB = SK / 2;           // code bytes per row and superstep: one 
 constexpr int BLK_CODE = 32 * ROWB;    // one 32-row block's codes per superstep (4 KiB)
 constexpr int LDS_BYTES = 160 * 1024;
 constexpr int MAX_SLOTS = 6;
+// Ring depth of units of at least this many operand blocks.  These units are planned for
+// launches that keep every CU busy; there, a shallower ring asks for fewer bytes at once when
+// all workgroups start together, so every CU's first superstep lands sooner (measured: 2x4
+// units with 3 slots instead of 5: 8 % less time on a 256-unit launch; 4x4 units 3 instead of
+// 4: 2.6 % less), while the smaller units, planned for small launches with few CUs busy,
+// keep the deeper ring that hides more latency (3 slots cost them up to 4 %).
+constexpr int LARGE_UNIT_BLOCKS = 6;
+constexpr int LARGE_UNIT_SLOTS = 3;
 
 // Chunk swizzle: row r of a block keeps its 16-byte chunk c at position c ^ swz(r).  The
 // 16-byte reads of one chunk from rows 0..7 (or 0..15) of a block then fall on distinct
@@ -105,7 +113,8 @@ struct Geo {
     static constexpr int SREG = 128 * (NBP + NAP) + 4;
     static constexpr int SCALE_AT = NBLK * BLK_CODE;
     static constexpr int SLOT = (SCALE_AT + 4 * SREG + 15) & ~15;
-    static constexpr int SLOTS = LDS_BYTES / SLOT > MAX_SLOTS ? MAX_SLOTS : LDS_BYTES / SLOT;
+    static constexpr int SLOT_CAP = NBLK >= LARGE_UNIT_BLOCKS ? LARGE_UNIT_SLOTS : MAX_SLOTS;
+    static constexpr int SLOTS = LDS_BYTES / SLOT > SLOT_CAP ? SLOT_CAP : LDS_BYTES / SLOT;
     static constexpr int NSI = (NBP + NAP) / 2;    // scale load instructions per wave
     static constexpr int OPS = NBLK + NSI;         // loads per wave and superstep
     static constexpr int NACC = NA * NB;           // accumulator blocks
