@@ -15,8 +15,8 @@ namespace nvfp4gg {
 // accumulation registers of a lane, up to 4 more in ordinary VGPRs).
 #define NVFP4GG_UNIT_SHAPES(X) \
     X(1, 1) X(1, 2) X(1, 4) X(1, 8) \
-    X(2, 1) X(2, 2) X(2, 4) X(2, 6) X(2, 8) X(2, 9) \
-    X(3, 2) X(3, 4) X(3, 5) X(3, 6) \
+    X(2, 1) X(2, 2) X(2, 3) X(2, 4) X(2, 5) X(2, 6) X(2, 8) X(2, 9) \
+    X(3, 2) X(3, 3) X(3, 4) X(3, 5) X(3, 6) \
     X(4, 1) X(4, 2) X(4, 3) X(4, 4) X(4, 5) \
     X(5, 2) X(5, 3) X(5, 4) \
     X(6, 1) X(6, 2) X(6, 3) \
