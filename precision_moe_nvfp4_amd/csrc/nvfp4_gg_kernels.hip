@@ -18,11 +18,14 @@
 //   * K runs in supersteps of 256 (128 bytes of codes per row: one cache line).  The four
 //     waves together fetch a superstep's lines (A and B codes, both scale sets) straight
 //     from HBM/L2 into a ring slot in LDS (direct-to-LDS buffer loads, one whole line per
-//     8 lanes); a 4- to 6-slot ring keeps 2-4 supersteps in flight.
+//     8 lanes); a ring of 3 slots (units of 6 or more operand blocks) to 6 slots keeps 2 to
+//     5 supersteps in flight.
 //   * Wave w consumes K values 64w .. 64w+63 of each superstep: each lane reads its 16
-//     code bytes per 32-row block with one LDS read (rows are stored with an XOR swizzle
-//     of their 16-byte chunks, so the reads are bank-conflict free) and its two scale
-//     bytes, converts them to MFMA fragments in registers and issues the MFMAs.  No LDS
+//     code bytes per 32-row block with one LDS read, or two 8-byte reads in the units with
+//     the most registers in use (rows are stored with an XOR swizzle of their 16-byte
+//     chunks, so the 16-byte reads are bank-conflict free; the 8-byte reads pair lanes on
+//     banks), and its two scale bytes, converts them to MFMA fragments in registers and
+//     issues the MFMAs.  No LDS
 //     holds converted values, so each FP4 byte is converted exactly once per unit.
 //   * One barrier per superstep publishes the next superstep and frees the slot that was
 //     read during the previous one.
