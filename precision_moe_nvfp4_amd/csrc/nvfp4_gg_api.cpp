@@ -79,13 +79,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //     ~33 (na + nb) conversion instructions (four FP4 conversions and four packed multiplies
 //     per fragment and step); an MFMA holds the issue port ~19 of its 32 cycles, so the
 //     conversions only partly hide behind it: ~110 na nb + 172 (na + nb) cycles per
-//     superstep, barrier and LDS reads included;
+//     superstep, barrier and LDS reads included; units of 11 operand blocks (their codes
+//     read in 8-byte halves, the exchange in the most rounds) measure ~400 more per superstep
+//     (with this term the short-K grouped shapes plan fewer of them: c3 -3 %, a 64-group
+//     MoE-like workload -2.6 %);
 //   * plus the pipeline fill (the first superstep's operands from HBM) and the epilogue
 //     (the four K-quarter partial tiles added through LDS, fp16 rounding, stores).
 double unit_cycles(int na, int nb, int k)
 {
     const double nm = (double)na * nb;
-    const double super = 110.0 * nm + 172.0 * (na + nb);
+    const double super = 110.0 * nm + 172.0 * (na + nb) + (na + nb >= 11 ? 400.0 : 0.0);
     const double nsup = (double)ceil_div(k, 256);
     return nsup * super + 8300.0 + 535.0 * nm;
 }
