@@ -86,13 +86,14 @@ constexpr int ROWB = SK / 2;           // code bytes per row and superstep: one 
 constexpr int BLK_CODE = 32 * ROWB;    // one 32-row block's codes per superstep (4 KiB)
 constexpr int LDS_BYTES = 160 * 1024;
 constexpr int MAX_SLOTS = 6;
-// Ring depth of units of at least this many operand blocks.  These units are planned for
-// launches that keep every CU busy; there, a shallower ring asks for fewer bytes at once when
-// all workgroups start together, so every CU's first superstep lands sooner (measured: 2x4
-// units with 3 slots instead of 5: 8 % less time on a 256-unit launch; 4x4 units 3 instead of
-// 4: 2.6 % less), while the smaller units, planned for small launches with few CUs busy,
-// keep the deeper ring that hides more latency (3 slots cost them up to 4 %).
-constexpr int LARGE_UNIT_BLOCKS = 6;
+// Ring depth of units of at least this many operand blocks (every shape but 1x1).  When many
+// CUs stream at once, a shallow ring keeps each CU's reads in flight on the supersteps needed
+// next and asks for fewer bytes when all workgroups start together, so every CU's superstep
+// lands sooner (measured: 3 slots instead of 5-6 cut 2x4 launches of 256 units by 9 %, 2x3 by
+// 10 %, 2x2 and 1x2 launches by 4-8 %, 4x4 units 3 instead of 4 by 3 %).  1x1 units, planned
+// for launches with few CUs busy, keep the deeper ring that hides more latency (3 slots cost
+// them up to 4 %).
+constexpr int LARGE_UNIT_BLOCKS = 3;
 constexpr int LARGE_UNIT_SLOTS = 3;
 
 // Chunk swizzle: row r of a block keeps its 16-byte chunk c at position c ^ swz(r).  The
