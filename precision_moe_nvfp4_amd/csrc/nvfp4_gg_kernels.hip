@@ -18,8 +18,7 @@
 //   * K runs in supersteps of 256 (128 bytes of codes per row: one cache line).  The four
 //     waves together fetch a superstep's lines (A and B codes, both scale sets) straight
 //     from HBM/L2 into a ring slot in LDS (direct-to-LDS buffer loads, one whole line per
-//     8 lanes); a ring of 3 slots (units of 6 or more operand blocks) to 6 slots keeps 2 to
-//     5 supersteps in flight.
+//     8 lanes); a ring of 3 slots (4 for 1x1 units) keeps 2 to 3 supersteps in flight.
 //   * Wave w consumes K values 64w .. 64w+63 of each superstep: each lane reads its 16
 //     code bytes per 32-row block with one LDS read, or two 8-byte reads in the units with
 //     the most registers in use (rows are stored with an XOR swizzle of their 16-byte
@@ -85,14 +84,14 @@ constexpr int SK = 256;                // K per superstep
 constexpr int ROWB = SK / 2;           // code bytes per row and superstep: one 128-byte line
 constexpr int BLK_CODE = 32 * ROWB;    // one 32-row block's codes per superstep (4 KiB)
 constexpr int LDS_BYTES = 160 * 1024;
-constexpr int MAX_SLOTS = 6;
+constexpr int MAX_SLOTS = 4;
 // Ring depth of units of at least this many operand blocks (every shape but 1x1).  When many
 // CUs stream at once, a shallow ring keeps each CU's reads in flight on the supersteps needed
 // next and asks for fewer bytes when all workgroups start together, so every CU's superstep
 // lands sooner (measured: 3 slots instead of 5-6 cut 2x4 launches of 256 units by 9 %, 2x3 by
 // 10 %, 2x2 and 1x2 launches by 4-8 %, 4x4 units 3 instead of 4 by 3 %).  1x1 units, planned
-// for launches with few CUs busy, keep the deeper ring that hides more latency (3 slots cost
-// them up to 4 %).
+// for launches with few CUs busy, take MAX_SLOTS: 4 hides their latency best (3 slots cost
+// them up to 2.6 %, 5 or 6 up to 5 %).
 constexpr int LARGE_UNIT_BLOCKS = 3;
 constexpr int LARGE_UNIT_SLOTS = 3;
 

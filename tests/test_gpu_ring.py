@@ -1,8 +1,7 @@
 """GPU parity at the edges of the LDS operand ring, for every compiled unit shape.
 
 A unit of NA x NB blocks streams K through a ring of S superstep slots in LDS (K = 256 each;
-S = 3 for units of 3 or more blocks, else up to 6 as the unit's operand bytes per superstep
-allow): the first S supersteps are issued up
+S = 3 for units of 3 or more blocks, 4 for 1x1 units): the first S supersteps are issued up
 front, and from then on the slot read during the previous superstep is refilled at every
 barrier, with a constant load wait in the steady state and shrinking ones in the last
 supersteps.  For every shape the kernel is compiled for (the planner's choice is overridden
@@ -34,10 +33,10 @@ def compiled_shapes():
 def ring_slots(na, nb):
     """Slots of the ring for a unit shape (the kernel's geometry: 4 KiB of codes per block and
     superstep, four scale regions of 128 B per even-rounded block plus 4 B, 160 KiB of LDS; at
-    most 3 slots for units of 3 or more blocks, else at most 6)."""
+    most 3 slots for units of 3 or more blocks, else at most 4)."""
     nbp, nap = (nb + 1) & ~1, (na + 1) & ~1
     slot = ((na + nb) * 4096 + 4 * (128 * (nbp + nap) + 4) + 15) & ~15
-    return min(3 if na + nb >= 3 else 6, (160 * 1024) // slot)
+    return min(3 if na + nb >= 3 else 4, (160 * 1024) // slot)
 
 
 SHAPES = compiled_shapes()
