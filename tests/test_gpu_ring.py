@@ -62,7 +62,7 @@ def test_ring_edges_every_shape(na, nb, monkeypatch):
         run_problems(probs, gg.SCALES_ROW_MAJOR)
 
 
-@pytest.mark.parametrize("na,nb", [(4, 4), (4, 5), (2, 9), (1, 1)])
+@pytest.mark.parametrize("na,nb", [(4, 4), (4, 5), (2, 9), (2, 4), (2, 3), (1, 2), (1, 1)])
 def test_ring_edges_blocked_scales(na, nb, monkeypatch):
     S = ring_slots(na, nb)
     monkeypatch.setenv("NVFP4_GG_FORCE_SHAPE", f"{na},{nb}")
