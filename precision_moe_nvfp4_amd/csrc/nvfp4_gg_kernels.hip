@@ -127,9 +127,9 @@ struct Geo {
     static constexpr bool FULL_READS = NACC < 20 && NBLK < 11;
     // epilogue exchange: per block, 4 element groups x 3 partner copies x 1 KiB
     static constexpr int RED_BLK = 3 * 4 * 1024;
-    // the exchange region starts after ring slots 0 .. SLOTS-2, which may meanwhile take the
-    // first supersteps of the workgroup's next unit
-    static constexpr int RED_AT = (SLOTS - 1) * SLOT;
+    // the exchange region starts after ring slot 0, which may meanwhile take the first
+    // superstep of the workgroup's next unit
+    static constexpr int RED_AT = SLOT;
     static constexpr int RED_FIT = (LDS_BYTES - RED_AT) / RED_BLK;
     static constexpr int RED_ROUND = RED_FIT < NACC ? RED_FIT : NACC;
     static_assert(RED_FIT >= 1, "the exchange region must hold one block");
@@ -591,9 +591,11 @@ struct Unit {
 };
 
 // Unit cu over the whole K of its group.  If `prefetched`, the previous unit already issued
-// this unit's supersteps 0 .. S-2 (same shape); if `pf_next`, this unit issues those of the
-// next unit nx (same shape) before its own epilogue, so that their fetch overlaps the
-// K reduction and the C stores.  All four waves run the same sequence of loads and barriers.
+// this unit's superstep 0 (same shape); if `pf_next`, this unit issues that of the next unit
+// nx (same shape) before its own epilogue, so that its fetch overlaps the K reduction and the
+// C stores.  (One superstep measured better than S-1 of them: a smaller burst while the
+// epilogue runs, and more LDS for the exchange.)  All four waves run the same sequence of
+// loads and barriers.
 template <int NA, int NB>
 __device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, const GroupArgs G, bool prefetched, bool pf_next,
                                          const Unit& nx, bool blocked, uint8_t* smem)
@@ -615,14 +617,15 @@ __device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, cons
     // superstep issues the same loads and waits with the same count)
     const auto kt_of = [&](int t) { return t < nsup - 1 ? gk::SK : t == nsup - 1 ? klast : 0; };
 
-    // The ring's first S supersteps go out first (only the last of them if the previous unit
-    // issued the others).  The previous unit's C stores may still be in flight: they touch
+    // The ring's first S supersteps go out first (superstep 0 only if the previous unit has
+    // not issued it).  The previous unit's C stores may still be in flight: they touch
     // neither LDS nor this unit's operands, and loads complete in issue order among
     // themselves, so whatever the stores do, the wait below means that superstep 0 has
     // landed.
     const UnitLoads<NA, NB> L = unit_loads<NA, NB>(G, k, row0, rows, col0, cols, blocked, wave, lane);
     if (!prefetched)
-        static_for<0, S - 1>([&](auto t) { issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave); });
+        issue_superstep<NA, NB>(L, smem, 0, kt_of(0), wave);
+    static_for<1, S - 1>([&](auto t) { issue_superstep<NA, NB>(L, smem + t * Gm::SLOT, t, kt_of(t), wave); });
     issue_superstep<NA, NB>(L, smem + (S - 1) * Gm::SLOT, S - 1, kt_of(S - 1), wave);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -737,18 +740,13 @@ __device__ __forceinline__ void run_unit(const KernArgs& A, const Unit& cu, cons
     wait_vm<0>();   // the zero refills beyond the last superstep have landed before the LDS is reused
 
     if (pf_next) {
-        // every wave has read the ring for the last time: slots 0 .. S-2 take the next unit's
-        // first supersteps (the exchange region lies beyond them)
+        // every wave has read the ring for the last time: slot 0 takes the next unit's first
+        // superstep (the exchange region lies beyond it)
         barrier_lds();
         const GroupArgs& Gn = A.grp[nx.gi];
-        const int nsup_n = (Gn.k + gk::SK - 1) / gk::SK;
-        const int klast_n = Gn.k - gk::SK * (nsup_n - 1);
         const UnitLoads<NA, NB> Ln =
             unit_loads<NA, NB>(Gn, Gn.k, nx.row0, nx.rows, nx.col0, nx.cols, blocked, wave, lane);
-        static_for<0, S - 1>([&](auto t) {
-            const int kt = t < nsup_n - 1 ? gk::SK : t == nsup_n - 1 ? klast_n : 0;
-            issue_superstep<NA, NB>(Ln, smem + t * Gm::SLOT, t, kt, wave);
-        });
+        issue_superstep<NA, NB>(Ln, smem, 0, Gn.k < gk::SK ? Gn.k : gk::SK, wave);   // K of superstep 0
     }
     drain_vgpr_acc<NA, NB>(acc);
     uint16_t* c0 = G.c + (long)row0 * ldc + col0;
